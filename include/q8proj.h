@@ -1,0 +1,178 @@
+/*
+ * q8proj -- Q8_0 quantized projections for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libq8proj.so. Sources of the operations:
+ *   [P1] "Part 4 - Lecture 05 - Fusion and the Activation-Quantization
+ *        Discipline" (jared-hpc AI inference engineer roadmap)
+ *   [P2] "54 - r51 - producer-fused A-quantize mode 1" (minfer)
+ *   [P3] "12 - r5-r6 re-ranking + structural rewrite spec" (minfer)
+ *
+ * Conventions for every entry point below:
+ *   - Pointers named in the argument lists are DEVICE pointers unless the
+ *     comment says "host". The caller owns every buffer; the library never
+ *     allocates, frees or caches device memory and keeps no state between
+ *     calls ([P1] section 4: pass the buffer, do not cache it).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls enqueue their kernels on it and return without synchronising.
+ *   - Arguments are validated on the host before anything is enqueued. On a
+ *     negative return nothing was launched and no output byte was written.
+ *   - Outputs must not alias inputs. Two consumers that must not overwrite
+ *     each other's quantized activation use separate buffers ([P1] s4).
+ *   - Calls with zero rows (rows == 0, T == 0, N == 0) are valid no-ops.
+ *   - No C++ exception crosses this interface.
+ *
+ * Data formats
+ *   q8_0 block: 32 elements, an f16 scale d and int8 values q, value = d*q
+ *   ([P1] s2.1, [P2] s2.1).
+ *
+ *   Quantized activations (written by q8_quantize / rmsnorm_quant /
+ *   swiglu_quant, read by q8_gemv and q8_gemm), for `rows` rows of width K:
+ *     Q8_LAYOUT_ROW      qs [rows][K] int8, row-major;
+ *                        sd [rows][K/32] uint32 = f16 bits of d | (uint16)ssum << 16,
+ *                        where ssum is the int16 sum of the block's 32 q ([P2] s2.1).
+ *     Q8_LAYOUT_PLANE64  tokens in groups of 64 ([P2] s2.1); with
+ *                        ntb = ceil(rows/64), nchunk = K/32:
+ *                        qs [ntb][nchunk][2048] int8: token r = t%64 of the group
+ *                          owns bytes [32r, 32r+32) of the tile; its 16-byte half
+ *                          h (elements 16h..16h+15 of the chunk) is stored at half
+ *                          position h ^ (((r>>2) ^ (r>>3)) & 1);
+ *                        sd [ntb][nchunk][64] uint32, same word as ROW, index r.
+ *                        Tokens rows <= t < 64*ntb are written as zero bytes
+ *                        ([P2] s3.1, the padded tail is part of the plane).
+ *
+ *   Weights (struct q8_weights) are Q8_0 split into two planes:
+ *     qs [N][K] int8 (row-major, 16-byte aligned) and d [N][K/32] f16 bits.
+ *   q8_weights_repack converts GGUF Q8_0 blocks (34 bytes: f16 d at +0, int8
+ *   qs[32] at +2, [P1] s2.1) into these planes once, at load time.
+ */
+#ifndef Q8PROJ_H
+#define Q8PROJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q8PROJ_ABI_VERSION 1
+
+/* return codes */
+#define Q8_OK 0
+#define Q8_EINVAL (-1)  /* NULL required pointer, unknown layout, m out of range */
+#define Q8_ESHAPE (-2)  /* negative size, K not a positive multiple of 32, K mismatch, ldc < N */
+#define Q8_EALIGN (-3)  /* pointer not aligned as documented */
+#define Q8_ELAUNCH (-4) /* the HIP runtime rejected a launch (hipGetLastError) */
+#define Q8_ENODEV (-5)  /* no usable gfx950 device for the calling thread */
+
+/* activation layouts */
+#define Q8_LAYOUT_ROW 0
+#define Q8_LAYOUT_PLANE64 1
+
+typedef struct q8_weights {
+    int64_t n;          /* output rows N */
+    int64_t k;          /* reduction width K, a positive multiple of 32 */
+    const int8_t* qs;   /* device, [N][K] int8, 16-byte aligned */
+    const uint16_t* d;  /* device, [N][K/32] f16 bits, 2-byte aligned */
+} q8_weights;
+
+/* ABI version (Q8PROJ_ABI_VERSION of the built library). */
+int q8_abi_version(void);
+
+/* Human-readable text of a return code (static storage). */
+const char* q8_strerror(int code);
+
+/*
+ * Bytes of the activation buffers for `rows` rows of width K in `layout`
+ * (host only, no device call). Writes *qs_bytes and *sd_bytes.
+ * Returns Q8_OK, Q8_EINVAL or Q8_ESHAPE.
+ */
+int q8_act_bytes(int64_t rows, int64_t k, int layout, size_t* qs_bytes, size_t* sd_bytes);
+
+/*
+ * Activation quantize ([P1] s3-s3.1: quantize once per activation and pass
+ * the buffer to every consumer; [P2] s3.2 quantize body).
+ * x: [rows][K] f32, 16-byte aligned. Per 32-element block:
+ *   amax = max|x|, d = amax/127 (f32, IEEE divide), q = rint(x/d) (IEEE
+ *   divide, ties to even) clamped to [-127, 127] (q = 0 when d == 0),
+ *   stored d = f16(d) (round to nearest even), ssum = sum(q).
+ * qs, sd: output buffers of q8_act_bytes(rows, K, layout); qs 16-byte and
+ * sd 4-byte aligned.
+ */
+int q8_quantize(const float* x, int64_t rows, int64_t k, int layout, int8_t* qs, uint32_t* sd, void* stream);
+
+/*
+ * Fused RMSNorm + quantize ([P2] s2.3, s3.1, s3.2: the producer writes the
+ * quantized activation in the same pass as its f32 output).
+ * y[t][j] = x[t][j] * (1/sqrt(mean_j x[t][j]^2 + eps)) * w[j], f32.
+ * The quantized output is q8_quantize applied to the y this call writes,
+ * bit for bit. qs == NULL and sd == NULL: f32 output only (then `layout` is
+ * ignored); either both or neither may be NULL.
+ * x, y: [rows][K] f32 (16-byte aligned), w: [K] f32 (16-byte aligned).
+ */
+int rmsnorm_quant(const float* x, const float* w, float eps, float* y, int64_t rows, int64_t k, int layout,
+                  int8_t* qs, uint32_t* sd, void* stream);
+
+/*
+ * Fused SwiGLU + quantize ([P2] s3.2): y = gate / (1 + e^-gate) * up, f32,
+ * and the quantized y as in rmsnorm_quant (NULL qs and sd: f32 only).
+ * gate, up, y: [rows][K] f32, 16-byte aligned.
+ */
+int swiglu_quant(const float* gate, const float* up, float* y, int64_t rows, int64_t k, int layout, int8_t* qs,
+                 uint32_t* sd, void* stream);
+
+/*
+ * Batch-1 Q8_0 GEMV ([P1] s2.1-s2.4): y[n] = sum_b f16(dw[n,b]) * f16(da[b]) * isum[n,b],
+ * isum[n,b] = sum_{j<32} qw[n,32b+j] * qa[32b+j] (exact int32).
+ * W: host pointer to the weight descriptor. a_qs, a_sd: one ROW-layout
+ * activation row of width W->k. y: [N] f32.
+ * The number of lanes per row follows K/32 and the rows per wave follow N
+ * (a dispatch threshold); every variant gives bit-identical y.
+ */
+int q8_gemv(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, float* y, void* stream);
+
+/*
+ * Several GEMVs that read the same activation, in one launch ([P1] s2.5,
+ * s6: one activation feeding q/k/v/g, generalised to unequal N).
+ * m: 1..4. W: host array of m host pointers, all with the same k. y: host
+ * array of m device pointers, y[i] of length W[i]->n. Each y[i] is
+ * bit-identical to q8_gemv(W[i], ...).
+ */
+int q8_gemv_shared_multi(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
+                         float* const* y, void* stream);
+
+/*
+ * Same as q8_gemv_shared_multi with the rows-per-wave factor forced
+ * (rows_per_wave in {0 = automatic, 1, 2, 4}); for tests and measurements.
+ */
+int q8_gemv_shared_multi_ex(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
+                            float* const* y, int rows_per_wave, void* stream);
+
+/*
+ * The GEMV launch plan for `total_rows` rows of width K (host only):
+ * lanes per row, rows per wave and the grid size in workgroups.
+ */
+int q8_gemv_plan(int64_t total_rows, int64_t k, int rows_per_wave, int* lanes_per_row, int* rows_per_wave_out,
+                 int64_t* workgroups);
+
+/*
+ * Prefill int8 GEMM ([P2] s2.1: the GEMM reads the pre-transposed quantized
+ * plane in bulk; [P3] s2-s3): C[t][n] = sum_b f16(da[t,b]) * f16(dw[n,b]) * isum[t,n,b].
+ * a_qs, a_sd: a PLANE64 activation of T tokens and width W->k.
+ * C: [T][ldc] f32, row-major, ldc >= N; only columns n < N of rows t < T are
+ * written.
+ */
+int q8_gemm(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t, float* c, int64_t ldc,
+            void* stream);
+
+/*
+ * Load-time conversion of GGUF Q8_0 blocks (device, [N][K/32] x 34 bytes,
+ * 2-byte aligned; [P1] s2.1) into the weight planes qs [N][K] and d [N][K/32]
+ * (device). Pure byte movement.
+ */
+int q8_weights_repack(const void* gguf_blocks, int64_t n, int64_t k, int8_t* qs, uint16_t* d, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

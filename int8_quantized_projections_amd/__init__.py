@@ -1,0 +1,23 @@
+"""Q8_0 quantized projections for AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library ``libq8proj.so`` (C ABI in
+``include/q8proj.h``). ``q8lib`` is a thin ctypes binding over it that only
+marshals torch tensors into pointers and the current HIP stream.
+"""
+from . import q8lib  # noqa: F401
+from .q8lib import (  # noqa: F401
+    LAYOUT_PLANE64,
+    LAYOUT_ROW,
+    Q8Error,
+    Q8Weights,
+    act_bytes,
+    alloc_act,
+    gemv_plan,
+    q8_gemm,
+    q8_gemv,
+    q8_gemv_shared_multi,
+    q8_quantize,
+    q8_weights_repack,
+    rmsnorm_quant,
+    swiglu_quant,
+)

@@ -1,0 +1,138 @@
+// Shared device helpers of the gfx950 Q8_0 projection kernels.
+//
+// Wave64 throughout. A q8_0 block of 32 f32 values is held by 8 consecutive
+// lanes, 4 values (one float4) per lane, so that every load and store of a
+// row is a fully coalesced 16-byte-per-lane access and the per-block
+// reductions (amax, ssum) are three DPP steps inside an 8-lane group.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q8proj.h"
+
+namespace q8 {
+
+constexpr int kQK = 32;          // elements per q8_0 block
+constexpr int kWave = 64;        // gfx950 wavefront size
+constexpr int kGroup = 64;       // tokens per PLANE64 group
+constexpr int kTileBytes = 2048; // qs bytes per (group, chunk) tile
+
+// DPP controls (gfx9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm:[1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm:[2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i inside each 8 lanes
+constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i inside each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                                 __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+// All-reduce over each aligned group of 8 lanes. After the two quad steps
+// every lane holds its quad's result; the half-mirror step pairs lane i with
+// lane 7-i, i.e. each quad with the other quad of its 8-lane group.
+__device__ __forceinline__ float max8(float a) {
+    a = fmaxf(a, dpp_f<kDppQuadXor1>(a));
+    a = fmaxf(a, dpp_f<kDppQuadXor2>(a));
+    a = fmaxf(a, dpp_f<kDppRowHalfMirror>(a));
+    return a;
+}
+
+__device__ __forceinline__ int sum8(int s) {
+    s += dpp_i<kDppQuadXor1>(s);
+    s += dpp_i<kDppQuadXor2>(s);
+    s += dpp_i<kDppRowHalfMirror>(s);
+    return s;
+}
+
+// Sum over all 64 lanes with a fixed tree; every lane receives the same bits.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<kDppQuadXor1>(v);
+    v += dpp_f<kDppQuadXor2>(v);
+    v += dpp_f<kDppRowHalfMirror>(v);
+    v += dpp_f<kDppRowMirror>(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t f16_bits(float d) {
+    _Float16 h = (_Float16)d;  // v_cvt_f16_f32, round to nearest even, f16 denormals kept
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_value(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
+}
+
+__device__ __forceinline__ int quant1(float x, float d) {
+    // IEEE-correct f32 division (the HIP default), rint (ties to even), clamp.
+    int q = (int)__builtin_rintf(x / d);
+    return min(127, max(-127, q));
+}
+
+struct Quant8 {
+    uint32_t qs4;  // this lane's 4 int8 values, little-endian
+    uint32_t sd;   // f16 bits of d | (uint16)ssum << 16, identical in all 8 lanes
+};
+
+// The one quantize body of the library ([P2] section 3.2, phase 2): every
+// producer (q8_quantize, rmsnorm_quant, swiglu_quant) calls it on the f32
+// values it has just produced, so their quantized outputs are bit-identical
+// by construction. The 8 lanes of an aligned group hold one 32-value block.
+__device__ __forceinline__ Quant8 quantize_block8(float4 v) {
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = max8(a);  // exact in any order
+    const float d = a / 127.0f;
+    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    if (d != 0.0f) {
+        q0 = quant1(v.x, d);
+        q1 = quant1(v.y, d);
+        q2 = quant1(v.z, d);
+        q3 = quant1(v.w, d);
+    }
+    const int s = sum8(q0 + q1 + q2 + q3);
+    Quant8 r;
+    r.qs4 = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+            ((uint32_t)(q3 & 0xFF) << 24);
+    r.sd = f16_bits(d) | ((uint32_t)(uint16_t)(int16_t)s << 16);
+    return r;
+}
+
+// PLANE64 addressing. Byte offset, inside the qs plane, of the 4-byte group
+// holding elements e..e+3 (e % 4 == 0) of chunk c of token t.
+__device__ __forceinline__ int64_t plane_qs_off(int64_t t, int c, int e, int nchunk) {
+    const int64_t g = t >> 6;
+    const int r = (int)(t & 63);
+    const int h = ((e >> 4) ^ (r >> 2) ^ (r >> 3)) & 1;
+    return (g * nchunk + c) * kTileBytes + r * 32 + h * 16 + (e & 15);
+}
+
+__device__ __forceinline__ int64_t plane_sd_idx(int64_t t, int c, int nchunk) {
+    return ((t >> 6) * nchunk + c) * kGroup + (t & 63);
+}
+
+}  // namespace q8
+
+// ---------------------------------------------------------------------------
+// Host-side helpers shared by the entry points.
+// ---------------------------------------------------------------------------
+namespace q8h {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? Q8_OK : Q8_ELAUNCH;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace q8h

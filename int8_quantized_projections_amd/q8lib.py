@@ -1,0 +1,230 @@
+"""ctypes binding of libq8proj.so (C ABI in include/q8proj.h).
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream, every step of the computation runs in the library's
+kernels. There is no CPU fallback: if the library is missing the functions
+raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libq8proj.so")
+
+LAYOUT_ROW = 0
+LAYOUT_PLANE64 = 1
+QK = 32
+
+_ERRORS = {0: "Q8_OK", -1: "Q8_EINVAL", -2: "Q8_ESHAPE", -3: "Q8_EALIGN", -4: "Q8_ELAUNCH", -5: "Q8_ENODEV"}
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {_ERRORS.get(code, code)} ({_lib_strerror(code)})")
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("qs", ctypes.c_void_p), ("d", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with argument types set. Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                              "python int8_quantized_projections_amd/_build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        wp = ctypes.POINTER(_Weights)
+        sig = {
+            "q8_abi_version": ([], ci),
+            "q8_strerror": ([ci], ctypes.c_char_p),
+            "q8_act_bytes": ([i64, i64, ci, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)], ci),
+            "q8_quantize": ([vp, i64, i64, ci, vp, vp, vp], ci),
+            "rmsnorm_quant": ([vp, vp, ctypes.c_float, vp, i64, i64, ci, vp, vp, vp], ci),
+            "swiglu_quant": ([vp, vp, vp, i64, i64, ci, vp, vp, vp], ci),
+            "q8_gemv": ([wp, vp, vp, vp, vp], ci),
+            "q8_gemv_shared_multi": ([ci, ctypes.POINTER(wp), vp, vp, ctypes.POINTER(vp), vp], ci),
+            "q8_gemv_shared_multi_ex": ([ci, ctypes.POINTER(wp), vp, vp, ctypes.POINTER(vp), ci, vp], ci),
+            "q8_gemv_plan": ([i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(i64)], ci),
+            "q8_gemm": ([wp, vp, vp, i64, vp, i64, vp], ci),
+            "q8_weights_repack": ([vp, i64, i64, vp, vp, vp], ci),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _lib_strerror(code: int) -> str:
+    try:
+        return lib().q8_strerror(code).decode()
+    except Exception:  # pragma: no cover - only when the library is absent
+        return "?"
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise Q8Error(rc, where)
+
+
+def _stream(device: torch.device | None = None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("q8lib expects device tensors")
+    if not t.is_contiguous():
+        raise ValueError("q8lib expects contiguous tensors")
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# Buffers
+# ---------------------------------------------------------------------------
+def act_bytes(rows: int, k: int, layout: int) -> tuple[int, int]:
+    q = ctypes.c_size_t()
+    s = ctypes.c_size_t()
+    _check(lib().q8_act_bytes(rows, k, layout, ctypes.byref(q), ctypes.byref(s)), "q8_act_bytes")
+    return q.value, s.value
+
+
+def alloc_act(rows: int, k: int, layout: int, device="cuda") -> tuple[torch.Tensor, torch.Tensor]:
+    """Caller-owned quantized-activation buffers (qs int8, sd int32 holding the uint32 words)."""
+    nq, ns = act_bytes(rows, k, layout)
+    return (torch.empty(nq, dtype=torch.int8, device=device), torch.empty(ns // 4, dtype=torch.int32, device=device))
+
+
+@dataclass
+class Q8Weights:
+    """Q8_0 weights as the library's two planes: qs [N, K] int8 and d [N, K/32] f16 bits (int16)."""
+    qs: torch.Tensor
+    d: torch.Tensor
+
+    @property
+    def n(self) -> int:
+        return self.qs.shape[0]
+
+    @property
+    def k(self) -> int:
+        return self.qs.shape[1]
+
+    def struct(self) -> _Weights:
+        return _Weights(self.n, self.k, _ptr(self.qs), _ptr(self.d))
+
+    def rows(self, start: int, stop: int) -> "Q8Weights":
+        """A band of output rows (a pointer offset and a smaller N)."""
+        return Q8Weights(self.qs[start:stop], self.d[start:stop])
+
+
+def q8_weights_repack(blocks: torch.Tensor, n: int, k: int) -> Q8Weights:
+    """GGUF Q8_0 blocks (device uint8, N*K/32*34 bytes) -> Q8Weights (one-time, at load)."""
+    assert blocks.dtype == torch.uint8 and blocks.numel() == n * (k // QK) * 34
+    qs = torch.empty((n, k), dtype=torch.int8, device=blocks.device)
+    d = torch.empty((n, k // QK), dtype=torch.int16, device=blocks.device)
+    _check(lib().q8_weights_repack(_ptr(blocks), n, k, _ptr(qs), _ptr(d), _stream(blocks.device)),
+           "q8_weights_repack")
+    return Q8Weights(qs, d)
+
+
+# ---------------------------------------------------------------------------
+# Producers
+# ---------------------------------------------------------------------------
+def _rows_k(x: torch.Tensor) -> tuple[int, int]:
+    if x.dim() == 1:
+        return 1, x.shape[0]
+    return x.shape[0], x.shape[-1]
+
+
+def q8_quantize(x: torch.Tensor, layout: int = LAYOUT_ROW, qs=None, sd=None):
+    rows, k = _rows_k(x)
+    if qs is None:
+        qs, sd = alloc_act(rows, k, layout, x.device)
+    _check(lib().q8_quantize(_ptr(x), rows, k, layout, _ptr(qs), _ptr(sd), _stream(x.device)), "q8_quantize")
+    return qs, sd
+
+
+def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float, layout: int = LAYOUT_ROW, y=None, qs=None, sd=None,
+                  quant: bool = True):
+    rows, k = _rows_k(x)
+    if y is None:
+        y = torch.empty_like(x)
+    if quant and qs is None:
+        qs, sd = alloc_act(rows, k, layout, x.device)
+    if not quant:
+        qs = sd = None
+    _check(lib().rmsnorm_quant(_ptr(x), _ptr(w), eps, _ptr(y), rows, k, layout, _ptr(qs), _ptr(sd),
+                               _stream(x.device)), "rmsnorm_quant")
+    return y, qs, sd
+
+
+def swiglu_quant(gate: torch.Tensor, up: torch.Tensor, layout: int = LAYOUT_ROW, y=None, qs=None, sd=None,
+                 quant: bool = True):
+    rows, k = _rows_k(gate)
+    if y is None:
+        y = torch.empty_like(gate)
+    if quant and qs is None:
+        qs, sd = alloc_act(rows, k, layout, gate.device)
+    if not quant:
+        qs = sd = None
+    _check(lib().swiglu_quant(_ptr(gate), _ptr(up), _ptr(y), rows, k, layout, _ptr(qs), _ptr(sd),
+                              _stream(gate.device)), "swiglu_quant")
+    return y, qs, sd
+
+
+# ---------------------------------------------------------------------------
+# Consumers
+# ---------------------------------------------------------------------------
+def q8_gemv(W: Q8Weights, a_qs: torch.Tensor, a_sd: torch.Tensor, y=None) -> torch.Tensor:
+    if y is None:
+        y = torch.empty(W.n, dtype=torch.float32, device=a_qs.device)
+    ws = W.struct()
+    _check(lib().q8_gemv(ctypes.byref(ws), _ptr(a_qs), _ptr(a_sd), _ptr(y), _stream(a_qs.device)), "q8_gemv")
+    return y
+
+
+def q8_gemv_shared_multi(Ws: list[Q8Weights], a_qs: torch.Tensor, a_sd: torch.Tensor, ys=None,
+                         rows_per_wave: int = 0) -> list[torch.Tensor]:
+    m = len(Ws)
+    if ys is None:
+        ys = [torch.empty(W.n, dtype=torch.float32, device=a_qs.device) for W in Ws]
+    structs = [W.struct() for W in Ws]
+    wps = (ctypes.POINTER(_Weights) * m)(*[ctypes.pointer(s) for s in structs])
+    yps = (ctypes.c_void_p * m)(*[_ptr(y) for y in ys])
+    _check(lib().q8_gemv_shared_multi_ex(m, wps, _ptr(a_qs), _ptr(a_sd), yps, rows_per_wave, _stream(a_qs.device)),
+           "q8_gemv_shared_multi")
+    return ys
+
+
+def gemv_plan(total_rows: int, k: int, rows_per_wave: int = 0) -> dict:
+    lanes = ctypes.c_int()
+    rows = ctypes.c_int()
+    wg = ctypes.c_int64()
+    _check(lib().q8_gemv_plan(total_rows, k, rows_per_wave, ctypes.byref(lanes), ctypes.byref(rows),
+                              ctypes.byref(wg)), "q8_gemv_plan")
+    return {"lanes_per_row": lanes.value, "rows_per_wave": rows.value, "workgroups": wg.value}
+
+
+def q8_gemm(W: Q8Weights, a_qs: torch.Tensor, a_sd: torch.Tensor, t: int, C=None, ldc: int | None = None):
+    if C is None:
+        C = torch.empty((t, W.n), dtype=torch.float32, device=a_qs.device)
+    if ldc is None:
+        ldc = C.shape[-1] if C.dim() > 1 else W.n
+    ws = W.struct()
+    _check(lib().q8_gemm(ctypes.byref(ws), _ptr(a_qs), _ptr(a_sd), t, _ptr(C), ldc, _stream(a_qs.device)), "q8_gemm")
+    return C

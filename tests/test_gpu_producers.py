@@ -1,0 +1,219 @@
+"""GPU parity of the producers against the oracle: q8_quantize, rmsnorm_quant,
+swiglu_quant (ROW and PLANE64), and the weight repack.
+
+Bars: quantized planes bit-exact with the oracle's quantize of the same f32
+input; producer f32 outputs within 1e-5 relative of the oracle's f64 value;
+fused planes bit-identical to the standalone quantize of the f32 output the
+same call wrote; padded plane tails zero on poisoned buffers.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _gpu import assert_rel, dev, ensure_built, poisoned, to_np, up, weights
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+ensure_built()
+from int8_quantized_projections_amd import q8lib  # noqa: E402
+
+ROW, PLANE = q8lib.LAYOUT_ROW, q8lib.LAYOUT_PLANE64
+
+
+def quantize_dev(x_dev, rows, K, layout):
+    nq, ns = q8lib.act_bytes(rows, K, layout)
+    qs = poisoned(nq, torch.int8)
+    sd = poisoned(ns // 4, torch.int32)
+    q8lib.q8_quantize(x_dev, layout, qs, sd)
+    return qs, sd
+
+
+def check_row_exact(qs, sd, x, what):
+    qo, do, so = oracle.quantize(x)
+    assert np.array_equal(to_np(qs).reshape(qo.shape), qo), f"{what}: qs differ"
+    sdo = oracle.pack_sd(do, so).view(np.int32)
+    assert np.array_equal(to_np(sd).reshape(sdo.shape), sdo), f"{what}: scales differ"
+
+
+def check_plane_exact(qs, sd, x, what):
+    T, K = x.shape
+    qo, do, so = oracle.quantize(x)
+    pq, psd = oracle.encode_plane64(qo, do, so, T, K)
+    gq, gsd = to_np(qs), to_np(sd).view(np.uint32)
+    assert np.array_equal(gq, pq), f"{what}: plane qs bytes differ ({np.sum(gq != pq)} bytes)"
+    assert np.array_equal(gsd, psd), f"{what}: plane scale words differ"
+    q2, d2, s2, bad = oracle.decode_plane64(gq, gsd, T, K)
+    assert bad == 0, f"{what}: padded tail not zero"
+
+
+def test_repack_matches_oracle_planes():
+    for N, K in ((5, 64), (97, 2080), (3, 32)):
+        Wf = synth.normal((N, K), stream=3000 + N, std=0.02)
+        W, wq, wd = weights(Wf)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(W.qs), wq)
+        assert np.array_equal(to_np(W.d).view(np.uint16), wd)
+
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (1, 128), (3, 2048), (7, 640), (5, 2080), (2, 7168), (4, 18944)])
+def test_quantize_row_bit_exact(rows, K):
+    x = synth.normal((rows, K), stream=3100 + K)
+    qs, sd = quantize_dev(up(x), rows, K, ROW)
+    torch.cuda.synchronize()
+    check_row_exact(qs, sd, x, f"q8_quantize ROW {rows}x{K}")
+
+
+@pytest.mark.parametrize("T,K", [(1, 32), (63, 96), (64, 640), (65, 896), (129, 256), (130, 3584)])
+def test_quantize_plane64_bit_exact_and_tail(T, K):
+    x = synth.normal((T, K), stream=3200 + T)
+    qs, sd = quantize_dev(up(x), T, K, PLANE)
+    torch.cuda.synchronize()
+    check_plane_exact(qs, sd, x, f"q8_quantize PLANE64 {T}x{K}")
+
+
+def test_quantize_edge_values_bit_exact():
+    """Ties, near-ties, zero blocks, f16-subnormal scales, f32-subnormal inputs."""
+    rng = np.random.default_rng(7)
+    blocks = []
+    # exact half-integers on a power-of-two scale (ties to even decide)
+    for k in (-8, 0, 3):
+        m = rng.integers(-126, 127, size=32) + 0.5
+        m[0] = 127.0
+        blocks.append(m * 2.0 ** k)
+    # values one f32 ulp either side of half-integers
+    base = (rng.integers(-120, 121, size=32) + 0.5).astype(np.float32)
+    base[0] = 127.0
+    blocks.append(np.nextafter(base, np.float32(np.inf)))
+    blocks.append(np.nextafter(base, np.float32(-np.inf)))
+    # zero block, single nonzero, negative amax
+    blocks.append(np.zeros(32))
+    z = np.zeros(32)
+    z[17] = -3.0
+    blocks.append(z)
+    # tiny scales: f16-subnormal d, f32-subnormal d, amax/127 underflowing to zero
+    for scale in (1e-6, 1e-38, 1e-42, 1e-45):
+        blocks.append(rng.standard_normal(32) * scale)
+    # random blocks at many magnitudes
+    for e in range(-30, 16, 3):
+        blocks.append(rng.standard_normal(32) * 2.0 ** e)
+    x = np.concatenate(blocks).astype(np.float32)
+    x = np.concatenate([x, np.zeros((-x.size) % 256, np.float32)]).reshape(1, -1)
+    qs, sd = quantize_dev(up(x), 1, x.shape[1], ROW)
+    torch.cuda.synchronize()
+    check_row_exact(qs, sd, x, "edge values")
+
+
+def test_quantize_random_many_rows_bit_exact():
+    x = synth.normal((333, 3584), stream=3300, std=3.0)
+    qs, sd = quantize_dev(up(x), 333, 3584, ROW)
+    pq, ps = quantize_dev(up(x), 333, 3584, PLANE)
+    torch.cuda.synchronize()
+    check_row_exact(qs, sd, x, "ROW 333x3584")
+    check_plane_exact(pq, ps, x, "PLANE64 333x3584")
+
+
+def test_quantize_zero_rows_is_noop_and_zero_row_is_zero_block():
+    qs = poisoned(64, torch.int8)
+    sd = poisoned(2, torch.int32)
+    x = torch.zeros(64, device=dev())
+    rc = q8lib.lib().q8_quantize(x.data_ptr(), 0, 64, ROW, qs.data_ptr(), sd.data_ptr(), None)
+    torch.cuda.synchronize()
+    assert rc == 0 and torch.all(qs.view(torch.uint8) == 0x5A) and torch.all(sd.view(torch.uint8) == 0x5A)
+    q8lib.q8_quantize(x, ROW, qs, sd)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(qs) == 0 and torch.count_nonzero(sd) == 0
+
+
+def check_plane_near_oracle(qs, sd, y_ref, layout, what):
+    """Decode the GPU's quantized output and compare it with the oracle's quantize of the
+    oracle's own f32-rounded reference y. The two f32 inputs may differ in the last bit, so a
+    few blocks may differ by one step; everything else must match exactly."""
+    T, K = y_ref.shape
+    gq, gsd = to_np(qs), to_np(sd).view(np.uint32)
+    if layout == PLANE:
+        q, d16, s, bad = oracle.decode_plane64(gq, gsd, T, K)
+        assert bad == 0, f"{what}: padded tail not zero"
+    else:
+        q = gq.reshape(T, K)
+        d16, s = oracle.unpack_sd(gsd.reshape(T, K // 32))
+    qo, do, so = oracle.quantize(y_ref.astype(np.float32))
+    blk_diff = np.any(q.reshape(T, -1, 32) != qo.reshape(T, -1, 32), axis=2) | (d16 != do)
+    assert blk_diff.mean() <= 0.01, f"{what}: {blk_diff.sum()} of {blk_diff.size} blocks differ"
+    assert np.abs(q.astype(int) - qo.astype(int)).max() <= 1, f"{what}: a value differs by more than one step"
+    assert np.abs(d16.astype(int) - do.astype(int)).max() <= 1, f"{what}: a scale differs by more than one ulp"
+    assert np.array_equal(s.astype(np.int64), q.reshape(T, -1, 32).astype(np.int64).sum(axis=2))
+
+
+def _rms_case(rows, K, layout, stream):
+    x = synth.normal((rows, K), stream=stream)
+    w = synth.normal((K,), stream=stream + 1, mean=1.0, std=0.1)
+    nq, ns = q8lib.act_bytes(rows, K, layout)
+    qs, sd = poisoned(nq, torch.int8), poisoned(ns // 4, torch.int32)
+    y = poisoned(rows * K, torch.float32).view(rows, K)
+    q8lib.rmsnorm_quant(up(x), up(w), 1e-6, layout, y, qs, sd)
+    y2 = poisoned(rows * K, torch.float32).view(rows, K)
+    q8lib.rmsnorm_quant(up(x), up(w), 1e-6, layout, y2, quant=False)
+    q2, s2 = quantize_dev(y, rows, K, layout)
+    torch.cuda.synchronize()
+    return x, w, y, qs, sd, y2, q2, s2
+
+
+@pytest.mark.parametrize("rows,K,layout", [(1, 7168, ROW), (1, 3584, ROW), (3, 640, ROW), (70, 896, PLANE),
+                                           (130, 3584, PLANE), (64, 256, PLANE), (3, 9216, ROW), (65, 18944, PLANE)])
+def test_rmsnorm_quant(rows, K, layout):
+    x, w, y, qs, sd, y2, q2, s2 = _rms_case(rows, K, layout, 3400 + K + rows)
+    ref = oracle.rmsnorm_f64(x, w, 1e-6)
+    assert_rel(to_np(y), ref, 1e-5, f"rmsnorm y {rows}x{K}")
+    # fused quantize == standalone quantize of the y this call wrote (bit for bit)
+    assert torch.equal(qs, q2) and torch.equal(sd, s2), "fused plane differs from q8_quantize(y)"
+    # the f32-only call writes the same y bits
+    assert torch.equal(y, y2), "f32-only call differs"
+    check_plane_near_oracle(qs, sd, ref, layout, f"rmsnorm quant {rows}x{K}")
+
+
+def _swiglu_case(rows, K, layout, stream):
+    g = synth.normal((rows, K), stream=stream)
+    u = synth.normal((rows, K), stream=stream + 1)
+    nq, ns = q8lib.act_bytes(rows, K, layout)
+    qs, sd = poisoned(nq, torch.int8), poisoned(ns // 4, torch.int32)
+    y = poisoned(rows * K, torch.float32).view(rows, K)
+    q8lib.swiglu_quant(up(g), up(u), layout, y, qs, sd)
+    y2 = poisoned(rows * K, torch.float32).view(rows, K)
+    q8lib.swiglu_quant(up(g), up(u), layout, y2, quant=False)
+    q2, s2 = quantize_dev(y, rows, K, layout)
+    torch.cuda.synchronize()
+    return g, u, y, qs, sd, y2, q2, s2
+
+
+@pytest.mark.parametrize("rows,K,layout", [(1, 128, ROW), (3, 640, ROW), (63, 896, PLANE), (64, 18944, PLANE),
+                                           (129, 2048, PLANE), (17, 96, ROW)])
+def test_swiglu_quant(rows, K, layout):
+    g, u, y, qs, sd, y2, q2, s2 = _swiglu_case(rows, K, layout, 3500 + K + rows)
+    ref = oracle.swiglu_f64(g, u)
+    assert_rel(to_np(y), ref, 1e-5, f"swiglu y {rows}x{K}")
+    assert torch.equal(qs, q2) and torch.equal(sd, s2), "fused plane differs from q8_quantize(y)"
+    assert torch.equal(y, y2), "f32-only call differs"
+    check_plane_near_oracle(qs, sd, ref, layout, f"swiglu quant {rows}x{K}")
+
+
+def test_swiglu_closed_form_points():
+    g = np.zeros((1, 32), np.float32)
+    u = np.ones((1, 32), np.float32)
+    g[0, 1] = 40.0
+    u[0, 2] = 0.0
+    g[0, 2] = 3.0
+    y, _, _ = q8lib.swiglu_quant(up(g), up(u), ROW, quant=False)
+    torch.cuda.synchronize()
+    yv = to_np(y)[0]
+    assert yv[0] == 0.0 and yv[2] == 0.0
+    assert abs(yv[1] - 40.0) <= 1e-5 * 40.0
+
+
+def test_producers_deterministic():
+    a = _rms_case(130, 3584, PLANE, 3600)
+    b = _rms_case(130, 3584, PLANE, 3600)
+    assert torch.equal(a[2], b[2]) and torch.equal(a[3], b[3]) and torch.equal(a[4], b[4])
