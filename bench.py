@@ -1,0 +1,482 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q8_0 projection path on one MI355X.
+
+Headline (one JSON line on stdout): the decode projection set at batch 1,
+H=7168 -- rmsnorm_quant (ROW) feeding q8_gemv_shared_multi over
+N=4096/512/512/4096, then q8_gemv N=12288 and N=96 on the same activation,
+then q8_quantize of a K=128 vector feeding q8_gemv N=4096 K=128. One step is
+those six launches; `value` is the step's algorithmic HBM bytes per second.
+Weights rotate over enough distinct copies (>= 1 GB) that no step finds its
+weights in the 256 MB Infinity Cache or the L2s. The steps are captured once
+in a HIP graph and replayed; inputs are resident in HBM before timing.
+
+Also measured (in "per_config"): the single 2048x2048 GEMV, the prefill
+rms-class and swiglu-class producers and q8 GEMMs at T=3325, and the LM head
+(GEMV at T=1, GEMM at T=512), each kernel timed with HIP events on its own
+stream, reported as GB/s or TOPS and as a fraction of the MI355X peaks.
+
+cpu_baseline: the CPU oracle computing the same decode step on this host,
+timed on a bounded number of steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q8_0 GEMV HBM GB/s (batch 1) + q8 GEMM i8 TOPS (prefill) vs roofline"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
+I8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
+EPS = 1e-6
+COLD_BYTES = 1.0e9      # rotate weight copies over at least this many bytes
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def ensure_built():
+    from int8_quantized_projections_amd import _build
+    import synth
+
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build()
+    if not os.path.exists(synth.LIB_PATH):
+        synth.build()
+
+
+# ---------------------------------------------------------------------------
+# Inputs on the device (weights quantized on the GPU by the library itself)
+# ---------------------------------------------------------------------------
+class Dev:
+    def __init__(self):
+        import torch
+        from int8_quantized_projections_amd import q8lib
+
+        self.torch = torch
+        self.q8 = q8lib
+        self.dev = torch.device("cuda:0")
+
+    def upload(self, a):
+        import numpy as np
+        return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+
+    def tensor(self, workload, name, rows=None):
+        import synth
+        return self.upload(synth.tensor(workload, name, rows))
+
+    def weights(self, workload, name, chunk_rows=16384):
+        """Q8_0 weights [N, K] from the workload's f32 draw, quantized on the GPU (q8_quantize, ROW)."""
+        import synth
+        torch, q8 = self.torch, self.q8
+        (N, K), _, _, _ = synth.WORKLOADS[workload]["tensors"][name]
+        qs = torch.empty((N, K), dtype=torch.int8, device=self.dev)
+        d = torch.empty((N, K // 32), dtype=torch.int16, device=self.dev)
+        for r0 in range(0, N, chunk_rows):
+            r1 = min(N, r0 + chunk_rows)
+            wf = self.tensor(workload, name, slice(r0, r1))
+            sd = torch.empty((r1 - r0) * (K // 32), dtype=torch.int32, device=self.dev)
+            q8.q8_quantize(wf, q8.LAYOUT_ROW, qs[r0:r1].reshape(-1), sd)
+            d[r0:r1] = sd.view(torch.int16).view(-1, 2)[:, 0].reshape(r1 - r0, K // 32)  # low half = f16 d
+            del wf, sd
+        torch.cuda.synchronize()
+        return q8.Q8Weights(qs, d)
+
+    def copies(self, W, n):
+        return [W] + [self.q8.Q8Weights(W.qs.clone(), W.d.clone()) for _ in range(n - 1)]
+
+
+def gemv_bytes(N, K):
+    """Algorithmic bytes of one batch-1 GEMV: weights (1.0625 B each), activation, output."""
+    return N * K + N * (K // 32) * 2 + K + (K // 32) * 4 + N * 4
+
+
+def quant_bytes(rows, K, layout=0):
+    qrows = rows if layout == 0 else (rows + 63) // 64 * 64
+    return rows * K * 4 + qrows * K + qrows * (K // 32) * 4
+
+
+def rms_bytes(rows, K, layout=0):
+    return quant_bytes(rows, K, layout) + rows * K * 4 + K * 4
+
+
+def swiglu_bytes(rows, K, layout=1):
+    return quant_bytes(rows, K, layout) + rows * K * 8
+
+
+def gemm_min_bytes(T, N, K):
+    qrows = (T + 63) // 64 * 64
+    return qrows * K + qrows * (K // 32) * 4 + N * K + N * (K // 32) * 2 + T * N * 4
+
+
+def stats(ms_list):
+    s = sorted(ms_list)
+    n = len(s)
+    pick = lambda q: s[min(n - 1, max(0, int(round(q * (n - 1)))))]
+    return {"median_us": pick(0.5) * 1e3, "p10_us": pick(0.1) * 1e3, "p90_us": pick(0.9) * 1e3,
+            "mean_us": sum(s) / n * 1e3, "reps": n}
+
+
+def time_each(D, fn, reps, warm=3):
+    """Device time of each call of fn(i), measured with HIP events on the current stream.
+    A spin kernel queued first keeps the stream busy while the host enqueues every
+    (event, launch, event) triple, so no host gap falls inside an interval."""
+    torch = D.torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda._sleep(int(2.4e9 * (1e-3 + 60e-6 * reps)))
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+# ---------------------------------------------------------------------------
+# Headline: decode projection set, H=7168
+# ---------------------------------------------------------------------------
+DEC_N = {"Wq": 4096, "Wk": 512, "Wv": 512, "Wg": 4096, "W12288": 12288, "W96": 96, "W128": 4096}
+
+
+def decode_step_bytes():
+    H = 7168
+    grouped = sum(gemv_bytes(DEC_N[n], H) for n in ("Wq", "Wk", "Wv", "Wg")) - 3 * (H + (H // 32) * 4)
+    parts = {
+        "rmsnorm_quant_row": rms_bytes(1, H),
+        "q8_gemv_shared_multi": grouped,
+        "q8_gemv_12288x7168": gemv_bytes(12288, H),
+        "q8_gemv_96x7168": gemv_bytes(96, H),
+        "q8_quantize_128": quant_bytes(1, 128),
+        "q8_gemv_4096x128": gemv_bytes(4096, 128),
+    }
+    return parts
+
+
+def bench_decode(D, steps, warmup, log_reps):
+    torch, q8 = D.torch, D.q8
+    wl = "decode_h7168"
+    H = 7168
+    log("[decode] building inputs")
+    x = D.tensor(wl, "x").view(1, H)
+    w = D.tensor(wl, "w_norm")
+    x128 = D.tensor(wl, "x128").view(1, 128)
+    base = {n: D.weights(wl, n) for n in DEC_N}
+    set_bytes = sum(W.qs.numel() + W.d.numel() * 2 for W in base.values())
+    ncopy = max(2, math.ceil(COLD_BYTES / set_bytes))
+    sets = [dict(zip(base, ws)) for ws in zip(*(D.copies(base[n], ncopy) for n in base))]
+    log(f"[decode] {ncopy} weight copies of {set_bytes / 1e6:.1f} MB")
+    y = torch.empty((1, H), device=D.dev)
+    aq, asd = q8.alloc_act(1, H, q8.LAYOUT_ROW)
+    bq, bsd = q8.alloc_act(1, 128, q8.LAYOUT_ROW)
+    outs = {n: torch.empty(DEC_N[n], device=D.dev) for n in DEC_N}
+
+    def launches(c):
+        S = sets[c % ncopy]
+        return [
+            ("rmsnorm_quant_row", lambda: q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_ROW, y, aq, asd)),
+            ("q8_gemv_shared_multi", lambda: q8.q8_gemv_shared_multi(
+                [S["Wq"], S["Wk"], S["Wv"], S["Wg"]], aq, asd, [outs["Wq"], outs["Wk"], outs["Wv"], outs["Wg"]])),
+            ("q8_gemv_12288x7168", lambda: q8.q8_gemv(S["W12288"], aq, asd, outs["W12288"])),
+            ("q8_gemv_96x7168", lambda: q8.q8_gemv(S["W96"], aq, asd, outs["W96"])),
+            ("q8_quantize_128", lambda: q8.q8_quantize(x128, q8.LAYOUT_ROW, bq, bsd)),
+            ("q8_gemv_4096x128", lambda: q8.q8_gemv(S["W128"], bq, bsd, outs["W128"])),
+        ]
+
+    def step(c):
+        for _, f in launches(c):
+            f()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # capture all timed steps in one graph (each step uses the next weight copy)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(i)
+    g.replay()  # untimed: graph upload / first replay
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    parts = decode_step_bytes()
+    step_bytes = sum(parts.values())
+
+    # per-kernel device time, HIP events around every launch (eager, rotating copies)
+    comp = {}
+    for idx, name in enumerate(parts):
+        t = time_each(D, lambda i, idx=idx: launches(i)[idx][1](), log_reps)
+        st = stats(t)
+        gbs = parts[name] / (st["mean_us"] * 1e-6) / 1e9
+        comp[name] = {**st, "bytes": parts[name], "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                      "launches_per_step": 1}
+    del g
+    return {"ms_per_step": ms / steps, "step_bytes": step_bytes, "value_GBps": step_bytes * steps / (ms * 1e-3) / 1e9,
+            "copies": ncopy, "components": comp, "launches_per_step": len(parts)}
+
+
+# ---------------------------------------------------------------------------
+# Other workloads (each kernel timed with events)
+# ---------------------------------------------------------------------------
+def bench_gemv2048(D, reps):
+    torch, q8 = D.torch, D.q8
+    wl = "gemv_2048"
+    x = D.tensor(wl, "x").view(1, 2048)
+    W = D.weights(wl, "W")
+    n = max(2, math.ceil(COLD_BYTES / (W.qs.numel() * 1.0625)))
+    Ws = D.copies(W, n)
+    aq, asd = q8.alloc_act(1, 2048, q8.LAYOUT_ROW)
+    y = torch.empty(2048, device=D.dev)
+    tq = stats(time_each(D, lambda i: q8.q8_quantize(x, q8.LAYOUT_ROW, aq, asd), reps))
+    tg = stats(time_each(D, lambda i: q8.q8_gemv(Ws[i % n], aq, asd, y), reps))
+    # back-to-back replay of many distinct-weight GEMVs: aggregate bytes / aggregate time
+    R = min(n, 200)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(R):
+            q8.q8_gemv(Ws[i], aq, asd, y)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    agg_us = e0.elapsed_time(e1) * 1e3 / R
+    gb = gemv_bytes(2048, 2048)
+    return {
+        "q8_quantize_2048": {**tq, "bytes": quant_bytes(1, 2048), "GBps": quant_bytes(1, 2048) / tq["mean_us"] / 1e3},
+        "q8_gemv_2048x2048": {**tg, "bytes": gb, "GBps": gb / tg["mean_us"] / 1e3,
+                              "frac_hbm": gb / tg["mean_us"] / 1e3 / HBM_PEAK_GBS},
+        "q8_gemv_2048x2048_graph_back_to_back": {"us_per_gemv": agg_us, "GBps": gb / agg_us / 1e3,
+                                                 "frac_hbm": gb / agg_us / 1e3 / HBM_PEAK_GBS, "gemvs": R},
+    }
+
+
+def gemm_entry(t, T, N, K):
+    ops = 2.0 * T * N * K
+    tops = ops / (t["mean_us"] * 1e-6) / 1e12
+    mb = gemm_min_bytes(T, N, K)
+    return {**t, "ops": ops, "TOPS": tops, "frac_i8_peak": tops / I8_PEAK_TOPS, "min_bytes": mb,
+            "GBps_min_bytes": mb / t["mean_us"] / 1e3}
+
+
+def bench_prefill_rms(D, reps):
+    torch, q8 = D.torch, D.q8
+    wl = "prefill_rms"
+    T, K = 3325, 3584
+    x = D.tensor(wl, "x")
+    w = D.tensor(wl, "w_norm")
+    Ws = {n: D.weights(wl, n) for n in ("Wq", "Wk", "Wv")}
+    y = torch.empty_like(x)
+    pq, ps = q8.alloc_act(T, K, q8.LAYOUT_PLANE64)
+    C = {n: torch.empty((T, W.n), device=D.dev) for n, W in Ws.items()}
+    out = {}
+    t = stats(time_each(D, lambda i: q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_PLANE64, y, pq, ps), reps))
+    b = rms_bytes(T, K, 1)
+    out["rmsnorm_quant_plane64"] = {**t, "bytes": b, "GBps": b / t["mean_us"] / 1e3,
+                                    "frac_hbm": b / t["mean_us"] / 1e3 / HBM_PEAK_GBS}
+    total_us = t["mean_us"]
+    for n, W in Ws.items():
+        t = stats(time_each(D, lambda i, W=W, n=n: q8.q8_gemm(W, pq, ps, T, C[n]), reps))
+        out[f"q8_gemm_{W.n}x{K}"] = gemm_entry(t, T, W.n, K)
+        total_us += t["mean_us"]
+    out["slice_tok_per_s"] = T / (total_us * 1e-6)
+    return out
+
+
+def bench_prefill_swiglu(D, reps):
+    torch, q8 = D.torch, D.q8
+    wl = "prefill_swiglu"
+    T, K, N = 3325, 18944, 3584
+    g = D.tensor(wl, "gate")
+    u = D.tensor(wl, "up")
+    W = D.weights(wl, "Wd")
+    y = torch.empty_like(g)
+    pq, ps = q8.alloc_act(T, K, q8.LAYOUT_PLANE64)
+    C = torch.empty((T, N), device=D.dev)
+    out = {}
+    t = stats(time_each(D, lambda i: q8.swiglu_quant(g, u, q8.LAYOUT_PLANE64, y, pq, ps), reps))
+    b = swiglu_bytes(T, K, 1)
+    out["swiglu_quant_plane64"] = {**t, "bytes": b, "GBps": b / t["mean_us"] / 1e3,
+                                   "frac_hbm": b / t["mean_us"] / 1e3 / HBM_PEAK_GBS}
+    t2 = stats(time_each(D, lambda i: q8.q8_gemm(W, pq, ps, T, C), reps))
+    out[f"q8_gemm_{N}x{K}"] = gemm_entry(t2, T, N, K)
+    out["slice_tok_per_s"] = T / ((t["mean_us"] + t2["mean_us"]) * 1e-6)
+    return out
+
+
+def bench_lm_head(D, reps):
+    torch, q8 = D.torch, D.q8
+    wl = "lm_head"
+    N, K = 152064, 3584
+    W = D.weights(wl, "W")
+    n = max(2, math.ceil(COLD_BYTES / (W.qs.numel() * 1.0625)))
+    Ws = D.copies(W, n)
+    w = D.tensor(wl, "w_norm")
+    x1 = D.tensor(wl, "x1")
+    x512 = D.tensor(wl, "x512")
+    out = {}
+    y1 = torch.empty_like(x1)
+    aq, asd = q8.alloc_act(1, K, q8.LAYOUT_ROW)
+    logits = torch.empty(N, device=D.dev)
+    t = stats(time_each(D, lambda i: q8.rmsnorm_quant(x1, w, EPS, q8.LAYOUT_ROW, y1, aq, asd), reps))
+    out["rmsnorm_quant_row_3584"] = {**t, "bytes": rms_bytes(1, K), "GBps": rms_bytes(1, K) / t["mean_us"] / 1e3}
+    tg = stats(time_each(D, lambda i: q8.q8_gemv(Ws[i % n], aq, asd, logits), reps))
+    gb = gemv_bytes(N, K)
+    out[f"q8_gemv_{N}x{K}"] = {**tg, "bytes": gb, "GBps": gb / tg["mean_us"] / 1e3,
+                                "frac_hbm": gb / tg["mean_us"] / 1e3 / HBM_PEAK_GBS}
+    out["t1_slice_tok_per_s"] = 1.0 / ((t["mean_us"] + tg["mean_us"]) * 1e-6)
+    T = 512
+    y512 = torch.empty_like(x512)
+    pq, ps = q8.alloc_act(T, K, q8.LAYOUT_PLANE64)
+    C = torch.empty((T, N), device=D.dev)
+    t = stats(time_each(D, lambda i: q8.rmsnorm_quant(x512, w, EPS, q8.LAYOUT_PLANE64, y512, pq, ps), reps))
+    out["rmsnorm_quant_plane64_512"] = {**t, "bytes": rms_bytes(T, K, 1),
+                                        "GBps": rms_bytes(T, K, 1) / t["mean_us"] / 1e3}
+    t2 = stats(time_each(D, lambda i: q8.q8_gemm(Ws[i % n], pq, ps, T, C), max(3, reps // 2)))
+    out[f"q8_gemm_{N}x{K}_T512"] = gemm_entry(t2, T, N, K)
+    out["t512_slice_tok_per_s"] = T / ((t["mean_us"] + t2["mean_us"]) * 1e-6)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle computing the decode step on this host
+# ---------------------------------------------------------------------------
+def cpu_baseline(budget_s=10.0, max_steps=200):
+    import numpy as np
+
+    import oracle
+    import synth
+
+    wl = "decode_h7168"
+    x = synth.tensor(wl, "x").reshape(1, -1)
+    w = synth.tensor(wl, "w_norm")
+    x128 = synth.tensor(wl, "x128").reshape(1, -1)
+    Wq = {}
+    for n in DEC_N:  # untimed: weights are quantized once, at load
+        q, d, _ = oracle.quantize(synth.tensor(wl, n))
+        Wq[n] = (q, d)
+
+    def step():
+        y = oracle.rmsnorm_f64(x, w, EPS).astype(np.float32)
+        aq, ad, _ = oracle.quantize(y)
+        for n in ("Wq", "Wk", "Wv", "Wg", "W12288", "W96"):
+            oracle.gemv(Wq[n][0], Wq[n][1], aq[0], ad[0])
+        bq, bd, _ = oracle.quantize(x128)
+        oracle.gemv(Wq["W128"][0], Wq["W128"][1], bq[0], bd[0])
+
+    step()  # warm
+    t0 = time.perf_counter()
+    k = 0
+    while k < max_steps and (time.perf_counter() - t0) < budget_s:
+        step()
+        k += 1
+    dt = time.perf_counter() - t0
+    step_bytes = sum(decode_step_bytes().values())
+    return {"value": step_bytes * k / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{k} full decode steps (rmsnorm + quantize + all 6 GEMV references, f64) in {dt:.1f} s; "
+                      "weights quantized once beforehand, untimed",
+            "ms_per_step": dt / k * 1e3}
+
+
+def traffic_for(kernel_key: str):
+    """Measured HBM traffic of a kernel from profiles/traffic.json, if the kernel's sources have
+    not changed since the counters were taken; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except Exception:
+        return None
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--reps", type=int, default=20, help="timed launches per kernel in the per-config section")
+    ap.add_argument("--configs", default="all", help="comma list of: decode,gemv2048,prefill_rms,prefill_swiglu,lm_head")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    ensure_built()
+    D = Dev()
+    torch = D.torch
+    torch.cuda.set_device(0)
+    which = set(["decode", "gemv2048", "prefill_rms", "prefill_swiglu", "lm_head"]) if args.configs == "all" \
+        else set(args.configs.split(","))
+    if "decode" not in which:
+        which.add("decode")
+
+    dec = bench_decode(D, args.steps, args.warmup, args.reps)
+    log(f"[decode] {dec['value_GBps']:.1f} GB/s, {dec['ms_per_step'] * 1e3:.2f} us/step")
+    per = {}
+    for name, fn in (("gemv2048", bench_gemv2048), ("prefill_rms", bench_prefill_rms),
+                     ("prefill_swiglu", bench_prefill_swiglu), ("lm_head", bench_lm_head)):
+        if name in which:
+            log(f"[{name}] running")
+            per[name] = fn(D, args.reps)
+            torch.cuda.empty_cache()
+    dom_name = "q8_gemv_12288x7168"
+    dom = dec["components"][dom_name]
+    achieved = dom["bytes"] / (dom["mean_us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(dom_name),
+                "algorithmic_bytes": dom["bytes"], "mean_launch_us": dom["mean_us"]}
+    cpu = None
+    if not args.no_cpu:
+        log("[cpu] timing the oracle")
+        cpu = cpu_baseline()
+    line = {
+        "metric": METRIC, "value": dec["value_GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": dec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": "decode_h7168", "batch": 1, "hidden": 7168,
+                   "gemvs": "rmsnorm_quant ROW -> shared_multi N=4096/512/512/4096; N=12288, N=96 (K=7168); "
+                            "q8_quantize K=128 -> N=4096 K=128",
+                   "launches_per_step": dec["launches_per_step"], "weight_copies": dec["copies"],
+                   "timing": "HIP graph of all timed steps, HIP events around the replay"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "components": dec["components"],
+        "per_config": per,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

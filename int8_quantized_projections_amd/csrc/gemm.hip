@@ -110,24 +110,46 @@ __global__ __launch_bounds__(256) void k_gemm(const int8_t* __restrict__ aq, con
     for (int c0 = 0; c0 < nb; c0 += kKT) {
         const int kc = min(kKT, nb - c0);
         __syncthreads();  // the previous stage's LDS reads are done
+        // Stage the A tile (kc chunks of the plane, copied verbatim) and its scales. All
+        // global loads are unconditional from clamped addresses so they issue together;
+        // only the LDS stores are predicated.
         {
             const uint4* src = reinterpret_cast<const uint4*>(plane + (int64_t)c0 * kTileBytes);
             uint4* dst = reinterpret_cast<uint4*>(lds_a);
-            for (int i = tid; i < kc * (kTileBytes / 16); i += 256) dst[i] = src[i];
+            const int na = kc * (kTileBytes / 16);
+            uint4 av[kKT * kTileBytes / 16 / 256];
+#pragma unroll
+            for (int it = 0; it < kKT * kTileBytes / 16 / 256; ++it) {
+                const int i = tid + 256 * it;
+                av[it] = src[i < na ? i : na - 1];
+            }
             const uint32_t* ssrc = splane + (int64_t)c0 * kGroup;
-            for (int i = tid; i < kc * kGroup; i += 256) lds_da[i] = f16_value(ssrc[i]);
+            const int ns = kc * kGroup;
+            uint32_t sv[kKT * kGroup / 256];
+#pragma unroll
+            for (int it = 0; it < kKT * kGroup / 256; ++it) {
+                const int i = tid + 256 * it;
+                sv[it] = ssrc[i < ns ? i : ns - 1];
+            }
+#pragma unroll
+            for (int it = 0; it < kKT * kTileBytes / 16 / 256; ++it) {
+                const int i = tid + 256 * it;
+                if (i < na) dst[i] = av[it];
+            }
+#pragma unroll
+            for (int it = 0; it < kKT * kGroup / 256; ++it) {
+                const int i = tid + 256 * it;
+                if (i < ns) lds_da[i] = f16_value(sv[it]);
+            }
         }
         v4i bf[kKT];
         float dwf[kKT];
 #pragma unroll
         for (int kb = 0; kb < kKT; ++kb) {
-            if (kb < kc && nvalid) {
-                bf[kb] = *reinterpret_cast<const v4i*>(wrow + (int64_t)(c0 + kb) * kQK);
-                dwf[kb] = f16_value(drow[c0 + kb]);
-            } else {
-                bf[kb] = v4i{0, 0, 0, 0};
-                dwf[kb] = 0.0f;
-            }
+            const int cb = c0 + kb < nb ? c0 + kb : nb - 1;
+            bf[kb] = *reinterpret_cast<const v4i*>(wrow + (int64_t)cb * kQK);
+            const uint16_t dbits = drow[cb];
+            dwf[kb] = (kb < kc && nvalid) ? f16_value(dbits) : 0.0f;
         }
         __syncthreads();
 #pragma unroll

@@ -36,6 +36,8 @@ struct GemvArgs {
     float* y[kMaxMats];
     int64_t off[kMaxMats];  // first global row of matrix i; INT64_MAX when unused
     int64_t total;          // total rows of all matrices
+    const int8_t* safe_q;   // row 0 of a non-empty matrix: the address rows past `total` load from
+    const uint16_t* safe_d;
 };
 
 // Row-wise all-reduce inside aligned groups of W lanes (W a power of two).
@@ -77,21 +79,19 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __res
     const int slot = lane / W, u = lane % W;
     const int nchunks = (nb + CH - 1) / CH;
 
+    // Every load below is unconditional from a clamped, always-valid address and the
+    // out-of-range contributions are zeroed afterwards: a load inside a divergent branch
+    // makes the compiler wait for it before the join, which serialises the stream.
     uint4 a0[NBL], a1[NBL];
     float da[NBL];
     auto load_act = [&](int ch) {
 #pragma unroll
         for (int j = 0; j < NBL; ++j) {
             const int b = ch * CH + u + j * W;
-            if (b < nb) {
-                a0[j] = *reinterpret_cast<const uint4*>(aq + (int64_t)b * kQK);
-                a1[j] = *reinterpret_cast<const uint4*>(aq + (int64_t)b * kQK + 16);
-                da[j] = f16_value(asd[b]);
-            } else {
-                a0[j] = make_uint4(0, 0, 0, 0);
-                a1[j] = a0[j];
-                da[j] = 0.0f;
-            }
+            const int bc = b < nb ? b : nb - 1;
+            a0[j] = *reinterpret_cast<const uint4*>(aq + (int64_t)bc * kQK);
+            a1[j] = *reinterpret_cast<const uint4*>(aq + (int64_t)bc * kQK + 16);
+            da[j] = f16_value(asd[bc]);
         }
     };
     if (nchunks == 1) load_act(0);
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __res
             float* yy = mi == 0 ? args.y[0] : mi == 1 ? args.y[1] : mi == 2 ? args.y[2] : args.y[3];
             const int64_t o = mi == 0 ? args.off[0] : mi == 1 ? args.off[1] : mi == 2 ? args.off[2] : args.off[3];
             const int64_t local = valid[r] ? row - o : 0;
-            wrow[r] = q + local * K;
-            drow[r] = d + local * nb;
+            wrow[r] = valid[r] ? q + local * K : args.safe_q;
+            drow[r] = valid[r] ? d + local * nb : args.safe_d;
             yout[r] = yy + local;
         }
         float acc[R];
@@ -123,28 +123,28 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __res
             if (nchunks > 1) load_act(ch);
             uint4 w0[R][NBL], w1[R][NBL];
             uint16_t dw[R][NBL];
+            bool inb[NBL];
+#pragma unroll
+            for (int j = 0; j < NBL; ++j) inb[j] = ch * CH + u + j * W < nb;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
 #pragma unroll
                 for (int j = 0; j < NBL; ++j) {
                     const int b = ch * CH + u + j * W;
-                    if (valid[r] && b < nb) {
-                        w0[r][j] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)b * kQK);
-                        w1[r][j] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)b * kQK + 16);
-                        dw[r][j] = drow[r][b];
-                    } else {
-                        w0[r][j] = make_uint4(0, 0, 0, 0);
-                        w1[r][j] = w0[r][j];
-                        dw[r][j] = 0;
-                    }
+                    const int bc = b < nb ? b : nb - 1;
+                    w0[r][j] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK);
+                    w1[r][j] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK + 16);
+                    dw[r][j] = drow[r][bc];
                 }
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
 #pragma unroll
                 for (int j = 0; j < NBL; ++j) {
+                    // blocks past K (a function of K only) add an exact zero
                     const int isum = dot32(w0[r][j], w1[r][j], a0[j], a1[j]);
-                    acc[r] = fmaf((float)isum, f16_value(dw[r][j]) * da[j], acc[r]);
+                    const float sc = inb[j] ? f16_value(dw[r][j]) * da[j] : 0.0f;
+                    acc[r] = fmaf((float)isum, sc, acc[r]);
                 }
             }
         }
@@ -268,6 +268,14 @@ int q8_gemv_shared_multi_ex(int m, const q8_weights* const* W, const int8_t* a_q
         a.off[i] = INT64_MAX;
     }
     a.total = total;
+    a.safe_q = nullptr;
+    a.safe_d = nullptr;
+    for (int i = m - 1; i >= 0; --i) {
+        if (W[i]->n > 0) {
+            a.safe_q = W[i]->qs;
+            a.safe_d = W[i]->d;
+        }
+    }
     if (a_qs == nullptr || a_sd == nullptr) return Q8_EINVAL;
     if (!q8h::aligned(a_qs, 16) || !q8h::aligned(a_sd, 4)) return Q8_EALIGN;
     if (total == 0) return Q8_OK;

@@ -40,7 +40,7 @@ __device__ __forceinline__ void store_quant(const Quant8& r, int64_t t, int c, i
 // is 8 consecutive blocks = 256 floats = one float4 per lane. Each wave does
 // UNR units, issuing all loads before any math.
 // ---------------------------------------------------------------------------
-constexpr int kUnr = 2;
+constexpr int kUnr = 4;
 constexpr int kWavesPerWg = 4;
 
 template <int D, bool SWIGLU>
@@ -54,133 +54,158 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
     const int sub = lane & 7;
     float4 v[kUnr], w[kUnr];
     int blk[kUnr];
+    // Unconditional loads from clamped, always-valid addresses (a load inside a
+    // divergent branch serialises the stream); padded rows read row 0 and are
+    // zeroed afterwards.
+    const int64_t trow = live ? t : 0;
 #pragma unroll
     for (int u = 0; u < kUnr; ++u) {
         blk[u] = (unit0 + u) * 8 + (lane >> 3);
-        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        w[u] = v[u];
-        if (live && blk[u] < nb) {
-            const int64_t off = t * K + (int64_t)blk[u] * kQK + sub * 4;
-            v[u] = *reinterpret_cast<const float4*>(a + off);
-            if constexpr (SWIGLU) w[u] = *reinterpret_cast<const float4*>(b + off);
-        }
+        const int bc = blk[u] < nb ? blk[u] : nb - 1;
+        const int64_t off = trow * K + (int64_t)bc * kQK + sub * 4;
+        v[u] = *reinterpret_cast<const float4*>(a + off);
+        if constexpr (SWIGLU) w[u] = *reinterpret_cast<const float4*>(b + off);
     }
+
 #pragma unroll
     for (int u = 0; u < kUnr; ++u) {
         if (blk[u] >= nb) continue;  // whole 8-lane groups drop out together
         if constexpr (SWIGLU) {
-            // [P2] s3.2: silu(g) * u with the plain expression.
+            // [P2] s3.2: silu(g) * u = g / (1 + e^-g) * u, with the hardware exp2 and
+            // reciprocal (each within about an ulp; the f32 output is checked to 1e-5).
             float4 o;
-            o.x = v[u].x / (1.0f + expf(-v[u].x)) * w[u].x;
-            o.y = v[u].y / (1.0f + expf(-v[u].y)) * w[u].y;
-            o.z = v[u].z / (1.0f + expf(-v[u].z)) * w[u].z;
-            o.w = v[u].w / (1.0f + expf(-v[u].w)) * w[u].w;
-            if (!live) o = make_float4(0.f, 0.f, 0.f, 0.f);
+            o.x = v[u].x * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].x)) * w[u].x;
+            o.y = v[u].y * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].y)) * w[u].y;
+            o.z = v[u].z * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].z)) * w[u].z;
+            o.w = v[u].w * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].w)) * w[u].w;
             if (live) *reinterpret_cast<float4*>(y + t * K + (int64_t)blk[u] * kQK + sub * 4) = o;
             v[u] = o;
         }
         if constexpr (D != kDstNone) {
-            const Quant8 r = quantize_block8(v[u]);  // padded rows hold zeros -> a zero block
+            // padded rows (which loaded row 0) quantize a zero block: all bytes zero
+            const Quant8 r = quantize_block8(live ? v[u] : make_float4(0.f, 0.f, 0.f, 0.f));
             store_quant<D>(r, t, blk[u], sub * 4, K, nb, qs, sd);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm + quantize. One wave per row; the row stays in registers (NV
-// float4 per lane, K <= 256*NV) between the sum of squares and the output,
-// so x is read once. Lane l holds float4 index l + 64 i; the 8 lanes
-// l = 8j..8j+7 of step i hold block 8i + j.
+// RMSNorm + quantize. WPR waves per row (1 for many rows, 4 when there are
+// few rows, so a decode row is spread over 256 lanes); the row stays in
+// registers (NV float4 per lane, K <= 256*WPR*NV) between the sum of squares
+// and the output, so x is read once, and w is loaded in the same wave of
+// loads. Lane i of the row (i = 64*(wave % WPR) + lane) holds float4 index
+// i + 64*WPR*k; 8 consecutive lanes hold one 32-value block.
 // NV == 0: rows wider than the register budget; x is read twice (the second
 // read hits L2), with the same per-lane order of the sum of squares.
 // ---------------------------------------------------------------------------
-template <int D, int NV>
+template <int D, int NV, int WPR>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, const float* __restrict__ w, float eps,
                                                  float* __restrict__ y, int64_t rows, int64_t tpad, int K, int nb,
                                                  int8_t* __restrict__ qs, uint32_t* __restrict__ sd) {
+    constexpr int kRowsPerWg = kWavesPerWg / WPR;
+    constexpr int kStride = kWave * WPR;  // float4 stride between a lane's elements
+    __shared__ float part[kWavesPerWg];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * kWavesPerWg + wave;
-    if (t >= tpad) return;  // uniform per wave
-    const int n4 = K >> 2;
-    const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x + t * K);
-    const float4* __restrict__ w4 = reinterpret_cast<const float4*>(w);
-    float4* __restrict__ y4 = reinterpret_cast<float4*>(y + t * K);
+    const int64_t t = (int64_t)blockIdx.x * kRowsPerWg + wave / WPR;
+    const int li = (wave % WPR) * kWave + lane;  // lane index inside the row
     const bool live = t < rows;
+    const bool inrow = t < tpad;  // uniform per wave
+    const int n4 = K >> 2;
+    const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x + (live ? t : 0) * K);
+    const float4* __restrict__ w4 = reinterpret_cast<const float4*>(w);
+    float4* __restrict__ y4 = reinterpret_cast<float4*>(y + (live ? t : 0) * K);
+
+    auto row_sum = [&](float ss) {
+        ss = wave_sum(ss);
+        if constexpr (WPR > 1) {
+            if (lane == 0) part[wave] = ss;
+            __syncthreads();
+            const int w0 = (wave / WPR) * WPR;
+            ss = part[w0];
+#pragma unroll
+            for (int i = 1; i < WPR; ++i) ss += part[w0 + i];
+        }
+        return ss;
+    };
 
     if constexpr (NV > 0) {
-        float4 v[NV];
+        float4 v[NV], wv[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int idx = li + kStride * k;
+            const int ic = idx < n4 ? idx : n4 - 1;
+            v[k] = x4[ic];
+            wv[k] = w4[ic];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep every x and w load ahead of the math
+        // masks applied only after every load is in flight
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            if (!live || li + kStride * k >= n4) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
         float ss = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = lane + kWave * i;
-            v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (live && idx < n4) v[i] = x4[idx];
+        for (int k = 0; k < NV; ++k) {
+            ss = fmaf(v[k].x, v[k].x, ss);
+            ss = fmaf(v[k].y, v[k].y, ss);
+            ss = fmaf(v[k].z, v[k].z, ss);
+            ss = fmaf(v[k].w, v[k].w, ss);
         }
-        if (live) {
+        ss = row_sum(ss);
+        if (!inrow) return;
+        // [P2] s3.2: scale = rsqrt(ss/d + eps), y = x * scale * w.
+        const float scale = rsqrtf(ss / (float)K + eps);
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                ss = fmaf(v[i].x, v[i].x, ss);
-                ss = fmaf(v[i].y, v[i].y, ss);
-                ss = fmaf(v[i].z, v[i].z, ss);
-                ss = fmaf(v[i].w, v[i].w, ss);
-            }
-            ss = wave_sum(ss);
-            // [P2] s3.2: scale = rsqrt(ss/d + eps), y = x * scale * w.
-            const float scale = rsqrtf(ss / (float)K + eps);
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int idx = lane + kWave * i;
-                if (idx < n4) {
-                    const float4 wv = w4[idx];
-                    float4 o;
-                    o.x = v[i].x * scale * wv.x;
-                    o.y = v[i].y * scale * wv.y;
-                    o.z = v[i].z * scale * wv.z;
-                    o.w = v[i].w * scale * wv.w;
-                    y4[idx] = o;
-                    v[i] = o;
-                }
-            }
+        for (int k = 0; k < NV; ++k) {
+            const int idx = li + kStride * k;
+            float4 o;
+            o.x = v[k].x * scale * wv[k].x;
+            o.y = v[k].y * scale * wv[k].y;
+            o.z = v[k].z * scale * wv[k].z;
+            o.w = v[k].w * scale * wv[k].w;
+            if (live && idx < n4) y4[idx] = o;
+            v[k] = o;  // zero for padded rows and past K
         }
         if constexpr (D != kDstNone) {
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int c = 8 * i + (lane >> 3);
+            for (int k = 0; k < NV; ++k) {
+                const int c = (li + kStride * k) >> 3;
                 if (c < nb) {
-                    const Quant8 r = quantize_block8(v[i]);
+                    const Quant8 r = quantize_block8(v[k]);
                     store_quant<D>(r, t, c, (lane & 7) * 4, K, nb, qs, sd);
                 }
             }
         }
     } else {
-        float scale = 0.0f;
+        float ss = 0.0f;
         if (live) {
-            float ss = 0.0f;
-            for (int idx = lane; idx < n4; idx += kWave) {
+            for (int idx = li; idx < n4; idx += kStride) {
                 const float4 a = x4[idx];
                 ss = fmaf(a.x, a.x, ss);
                 ss = fmaf(a.y, a.y, ss);
                 ss = fmaf(a.z, a.z, ss);
                 ss = fmaf(a.w, a.w, ss);
             }
-            ss = wave_sum(ss);
-            scale = rsqrtf(ss / (float)K + eps);
         }
-        const int steps = (n4 + kWave - 1) / kWave;
-        for (int i = 0; i < steps; ++i) {
-            const int idx = lane + kWave * i;
-            const int c = 8 * i + (lane >> 3);
+        ss = row_sum(ss);
+        if (!inrow) return;
+        const float scale = rsqrtf(ss / (float)K + eps);
+        const int steps = (n4 + kStride - 1) / kStride;
+        for (int k = 0; k < steps; ++k) {
+            const int idx = li + kStride * k;
+            const int ic = idx < n4 ? idx : n4 - 1;
+            const float4 a = x4[ic];
+            const float4 wq = w4[ic];
             float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
             if (live && idx < n4) {
-                const float4 a = x4[idx];
-                const float4 wv = w4[idx];
-                o.x = a.x * scale * wv.x;
-                o.y = a.y * scale * wv.y;
-                o.z = a.z * scale * wv.z;
-                o.w = a.w * scale * wv.w;
+                o.x = a.x * scale * wq.x;
+                o.y = a.y * scale * wq.y;
+                o.z = a.z * scale * wq.z;
+                o.w = a.w * scale * wq.w;
                 y4[idx] = o;
             }
             if constexpr (D != kDstNone) {
+                const int c = idx >> 3;
                 if (c < nb) {
                     const Quant8 r = quantize_block8(o);
                     store_quant<D>(r, t, c, (lane & 7) * 4, K, nb, qs, sd);
@@ -246,12 +271,12 @@ int launch_elementwise(const float* a, const float* b, float* y, int64_t rows, i
     return q8h::launch_status();
 }
 
-template <int D>
+template <int D, int WPR>
 void launch_rms(int nv, dim3 grid, hipStream_t s, const float* x, const float* w, float eps, float* y, int64_t rows,
                 int64_t tpad, int k, int nb, int8_t* qs, uint32_t* sd) {
-#define Q8_RMS_CASE(N)                                                                                         \
-    case N:                                                                                                    \
-        hipLaunchKernelGGL((k_rmsnorm<D, N>), grid, dim3(256), 0, s, x, w, eps, y, rows, tpad, k, nb, qs, sd); \
+#define Q8_RMS_CASE(N)                                                                                              \
+    case N:                                                                                                         \
+        hipLaunchKernelGGL((k_rmsnorm<D, N, WPR>), grid, dim3(256), 0, s, x, w, eps, y, rows, tpad, k, nb, qs, sd); \
         break;
     switch (nv) {
         Q8_RMS_CASE(1)
@@ -263,17 +288,36 @@ void launch_rms(int nv, dim3 grid, hipStream_t s, const float* x, const float* w
         Q8_RMS_CASE(24)
         Q8_RMS_CASE(32)
         default:
-            hipLaunchKernelGGL((k_rmsnorm<D, 0>), grid, dim3(256), 0, s, x, w, eps, y, rows, tpad, k, nb, qs, sd);
+            hipLaunchKernelGGL((k_rmsnorm<D, 0, WPR>), grid, dim3(256), 0, s, x, w, eps, y, rows, tpad, k, nb, qs,
+                               sd);
     }
 #undef Q8_RMS_CASE
 }
 
-int rms_nv(int64_t k) {
-    const int64_t need = q8h::ceil_div(k / 4, kWave);
+// Float4 registers per lane for a row of width k spread over wpr waves
+// (0 = too wide for registers: the two-pass form).
+int rms_nv(int64_t k, int wpr) {
+    const int64_t need = q8h::ceil_div(k / 4, (int64_t)kWave * wpr);
     const int steps[] = {1, 2, 4, 8, 12, 16, 24, 32};
     for (int v : steps)
         if (need <= v) return v;
     return 0;
+}
+
+// Waves per row: spread a row over 4 waves when there are too few rows to
+// fill the GPU with one wave per row.
+int rms_wpr(int64_t rows) { return rows < 1024 ? 4 : 1; }
+
+template <int D>
+void dispatch_rms(hipStream_t s, const float* x, const float* w, float eps, float* y, int64_t rows, int64_t tpad,
+                  int k, int nb, int8_t* qs, uint32_t* sd) {
+    const int wpr = rms_wpr(rows);
+    const int nv = rms_nv(k, wpr);
+    const dim3 grid((unsigned)q8h::ceil_div(tpad, kWavesPerWg / wpr));
+    if (wpr == 4)
+        launch_rms<D, 4>(nv, grid, s, x, w, eps, y, rows, tpad, k, nb, qs, sd);
+    else
+        launch_rms<D, 1>(nv, grid, s, x, w, eps, y, rows, tpad, k, nb, qs, sd);
 }
 
 }  // namespace
@@ -333,15 +377,14 @@ int rmsnorm_quant(const float* x, const float* w, float eps, float* y, int64_t r
     if (!q8h::aligned(x, 16) || !q8h::aligned(w, 16) || !q8h::aligned(y, 16)) return Q8_EALIGN;
     const int64_t tpad = (qs == nullptr) ? rows : padded_rows(rows, layout);
     if (tpad == 0) return Q8_OK;
-    const dim3 grid((unsigned)q8h::ceil_div(tpad, kWavesPerWg));
-    const int nv = rms_nv(k), nb = (int)(k / kQK);
+    const int nb = (int)(k / kQK);
     hipStream_t s = (hipStream_t)stream;
     if (qs == nullptr)
-        launch_rms<kDstNone>(nv, grid, s, x, w, eps, y, rows, tpad, (int)k, nb, qs, sd);
+        dispatch_rms<kDstNone>(s, x, w, eps, y, rows, tpad, (int)k, nb, qs, sd);
     else if (layout == Q8_LAYOUT_ROW)
-        launch_rms<kDstRow>(nv, grid, s, x, w, eps, y, rows, tpad, (int)k, nb, qs, sd);
+        dispatch_rms<kDstRow>(s, x, w, eps, y, rows, tpad, (int)k, nb, qs, sd);
     else
-        launch_rms<kDstPlane>(nv, grid, s, x, w, eps, y, rows, tpad, (int)k, nb, qs, sd);
+        dispatch_rms<kDstPlane>(s, x, w, eps, y, rows, tpad, (int)k, nb, qs, sd);
     return q8h::launch_status();
 }
 

@@ -72,11 +72,10 @@ __device__ __forceinline__ float f16_value(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
 }
 
-__device__ __forceinline__ int quant1(float x, float d) {
-    // IEEE-correct f32 division (the HIP default), rint (ties to even), clamp.
-    int q = (int)__builtin_rintf(x / d);
-    return min(127, max(-127, q));
-}
+// True when z is within 2^-14 of a half-integer (n = rint(z)).
+__device__ __forceinline__ bool near_half(float z, float n) { return fabsf(fabsf(z - n) - 0.5f) <= 0x1p-14f; }
+
+__device__ __forceinline__ int clamp127(float n) { return min(127, max(-127, (int)n)); }
 
 struct Quant8 {
     uint32_t qs4;  // this lane's 4 int8 values, little-endian
@@ -87,23 +86,34 @@ struct Quant8 {
 // producer (q8_quantize, rmsnorm_quant, swiglu_quant) calls it on the f32
 // values it has just produced, so their quantized outputs are bit-identical
 // by construction. The 8 lanes of an aligned group hold one 32-value block.
+//
+// q = rint(x / d) with x/d the correctly rounded f32 quotient, computed
+// exactly but cheaply: z = x * rcp(d) is within 2^-15 of x/d for |x/d| <= 128
+// (v_rcp_f32 is within 1 ulp, plus two roundings), so rint(z) == rint(x/d)
+// unless z lies within 2^-14 of a half-integer; those lanes (and blocks with
+// an f32-subnormal d) redo the four values with the IEEE division.
 __device__ __forceinline__ Quant8 quantize_block8(float4 v) {
     float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     a = max8(a);  // exact in any order
     const float d = a / 127.0f;
-    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-    if (d != 0.0f) {
-        q0 = quant1(v.x, d);
-        q1 = quant1(v.y, d);
-        q2 = quant1(v.z, d);
-        q3 = quant1(v.w, d);
+    const float r = d != 0.0f ? __builtin_amdgcn_rcpf(d) : 0.0f;  // d == 0: all q are 0
+    const float z0 = v.x * r, z1 = v.y * r, z2 = v.z * r, z3 = v.w * r;
+    float n0 = __builtin_rintf(z0), n1 = __builtin_rintf(z1), n2 = __builtin_rintf(z2), n3 = __builtin_rintf(z3);
+    const int slow = (int)(d != 0.0f && d < 0x1p-126f) | (int)near_half(z0, n0) | (int)near_half(z1, n1) |
+                     (int)near_half(z2, n2) | (int)near_half(z3, n3);
+    if (slow) {
+        n0 = __builtin_rintf(v.x / d);
+        n1 = __builtin_rintf(v.y / d);
+        n2 = __builtin_rintf(v.z / d);
+        n3 = __builtin_rintf(v.w / d);
     }
+    const int q0 = clamp127(n0), q1 = clamp127(n1), q2 = clamp127(n2), q3 = clamp127(n3);
     const int s = sum8(q0 + q1 + q2 + q3);
-    Quant8 r;
-    r.qs4 = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
-            ((uint32_t)(q3 & 0xFF) << 24);
-    r.sd = f16_bits(d) | ((uint32_t)(uint16_t)(int16_t)s << 16);
-    return r;
+    Quant8 res;
+    res.qs4 = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+              ((uint32_t)(q3 & 0xFF) << 24);
+    res.sd = f16_bits(d) | ((uint32_t)(uint16_t)(int16_t)s << 16);
+    return res;
 }
 
 // PLANE64 addressing. Byte offset, inside the qs plane, of the 4-byte group

@@ -53,7 +53,7 @@ def test_gemm_matches_oracle_every_cell(T, N, K):
 
 @pytest.mark.parametrize("T,N,K", [(70, 129, 18944), (64, 128, 3584), (3, 200, 640)])
 def test_gemm_exact_power_of_two_scales(T, N, K):
-    h = int(oracle.f32_to_f16_bits(np.float32(2.0 ** -6)))
+    h = int(oracle.f32_to_f16_bits(np.float32(2.0 ** -6)).reshape(-1)[0])
     aq = synth.uniform_i8((T, K), stream=5100, lo=-15, hi=15)
     wq = synth.uniform_i8((N, K), stream=5101, lo=-15, hi=15)
     ad = np.full((T, K // 32), h, np.uint16)

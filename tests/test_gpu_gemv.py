@@ -61,7 +61,7 @@ def test_gemv_variants_bit_identical(N, K):
 def test_gemv_exact_power_of_two_scales(N, K):
     """All scales 2^-6, |q| <= 15: every partial sum is exact, so y must equal the
     exact integer dot product times 2^-12 bit for bit -- this pins the int32 block sums."""
-    h = int(oracle.f32_to_f16_bits(np.float32(2.0 ** -6)))
+    h = int(oracle.f32_to_f16_bits(np.float32(2.0 ** -6)).reshape(-1)[0])
     aq = synth.uniform_i8((1, K), stream=4200, lo=-15, hi=15)
     wq = synth.uniform_i8((N, K), stream=4201, lo=-15, hi=15)
     ad = np.full((1, K // 32), h, np.uint16)
