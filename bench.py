@@ -363,7 +363,7 @@ def bench_lm_head(D, reps):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle computing the decode step on this host
 # ---------------------------------------------------------------------------
-def cpu_baseline(budget_s=10.0, max_steps=200):
+def cpu_baseline(budget_s=10.0, max_steps=100000):
     import numpy as np
 
     import oracle
@@ -400,6 +400,23 @@ def cpu_baseline(budget_s=10.0, max_steps=200):
             "ms_per_step": dt / k * 1e3}
 
 
+def hbm_reference(D, mib=1024, reps=5):
+    """Practical bandwidth of plain device copies and reads on this GPU (context for the
+    fractions; the copy kernel also calibrates the HBM byte counters)."""
+    torch = D.torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device=D.dev)
+    dst = torch.empty_like(src)
+    tc = stats(time_each(D, lambda i: dst.copy_(src), reps))
+    tr = stats(time_each(D, lambda i: torch.sum(src), reps))
+    out = {"copy_bytes": 2 * n * 4, "copy_GBps": 2 * n * 4 / tc["mean_us"] / 1e3,
+           "read_bytes": n * 4, "read_GBps": n * 4 / tr["mean_us"] / 1e3,
+           "kernels": "torch copy_ and sum of a %d MiB f32 buffer" % mib}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def traffic_for(kernel_key: str):
     """Measured HBM traffic of a kernel from profiles/traffic.json, if the kernel's sources have
     not changed since the counters were taken; else None."""
@@ -428,6 +445,7 @@ def main():
     ap.add_argument("--reps", type=int, default=20, help="timed launches per kernel in the per-config section")
     ap.add_argument("--configs", default="all", help="comma list of: decode,gemv2048,prefill_rms,prefill_swiglu,lm_head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall-clock budget of the oracle CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -439,9 +457,16 @@ def main():
     torch.cuda.set_device(0)
     which = set(["decode", "gemv2048", "prefill_rms", "prefill_swiglu", "lm_head"]) if args.configs == "all" \
         else set(args.configs.split(","))
-    if "decode" not in which:
-        which.add("decode")
+    if "decode" not in which:  # profiling a subset: no headline line
+        for name, fn in (("gemv2048", bench_gemv2048), ("prefill_rms", bench_prefill_rms),
+                         ("prefill_swiglu", bench_prefill_swiglu), ("lm_head", bench_lm_head)):
+            if name in which:
+                log(f"[{name}] running")
+                print(json.dumps({name: fn(D, args.reps)}), flush=True)
+        return
 
+    hbm = hbm_reference(D)
+    log(f"[hbm] copy {hbm['copy_GBps']:.0f} GB/s, read {hbm['read_GBps']:.0f} GB/s")
     dec = bench_decode(D, args.steps, args.warmup, args.reps)
     log(f"[decode] {dec['value_GBps']:.1f} GB/s, {dec['ms_per_step'] * 1e3:.2f} us/step")
     per = {}
@@ -460,7 +485,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("[cpu] timing the oracle")
-        cpu = cpu_baseline()
+        cpu = cpu_baseline(budget_s=args.cpu_seconds)
     line = {
         "metric": METRIC, "value": dec["value_GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": dec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -472,6 +497,7 @@ def main():
                    "timing": "HIP graph of all timed steps, HIP events around the replay"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "hbm_reference": hbm,
         "components": dec["components"],
         "per_config": per,
     }

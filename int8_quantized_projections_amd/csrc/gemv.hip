@@ -178,11 +178,12 @@ Plan make_plan(int64_t total, int nb, int force_rows) {
     const int64_t slots = q8h::ceil_div(total, kWave / p.lanes);
     // [P1] s2.3: several rows per wave reuse the activation but divide the
     // grid; only take them when the grid stays large (threshold re-derived for
-    // 256 CUs: keep at least 1024 row groups).
+    // 256 CUs: two rows per wave from 2048 row slots on; four rows per wave
+    // measured no faster and need 228 VGPRs, so they are only used on request).
     if (force_rows > 0)
         p.rows = force_rows;
     else
-        p.rows = slots >= 4 * 1024 ? 4 : slots >= 2 * 1024 ? 2 : 1;
+        p.rows = slots >= 2048 ? 2 : 1;
     p.groups = q8h::ceil_div(slots, p.rows);
     const int64_t waves = p.groups < kMaxWaves ? p.groups : kMaxWaves;
     p.workgroups = q8h::ceil_div(waves, kWavesPerWg);

@@ -127,8 +127,8 @@ def test_gemv_rows_per_wave_threshold(L):
     assert q8lib.gemv_plan(2047, 7168)["rows_per_wave"] == 1
     assert q8lib.gemv_plan(2048, 7168)["rows_per_wave"] == 2
     assert q8lib.gemv_plan(4095, 7168)["rows_per_wave"] == 2
-    assert q8lib.gemv_plan(4096, 7168)["rows_per_wave"] == 4
-    assert q8lib.gemv_plan(12288, 7168)["rows_per_wave"] == 4
+    assert q8lib.gemv_plan(12288, 7168)["rows_per_wave"] == 2
+    assert q8lib.gemv_plan(12288, 7168, rows_per_wave=4)["rows_per_wave"] == 4
     # narrow rows share a wave: K=128 puts 16 rows in a wave, so 4096 rows give 256 slots
     p = q8lib.gemv_plan(4096, 128)
     assert p["lanes_per_row"] == 4 and p["rows_per_wave"] == 1
