@@ -2,10 +2,11 @@
 """Benchmark of the Q8_0 projection path on one MI355X.
 
 Headline (one JSON line on stdout): the decode projection set at batch 1,
-H=7168 -- rmsnorm_quant (ROW) feeding q8_gemv_shared_multi over
-N=4096/512/512/4096, then q8_gemv N=12288 and N=96 on the same activation,
-then q8_quantize of a K=128 vector feeding q8_gemv N=4096 K=128. One step is
-those six launches; `value` is the step's algorithmic HBM bytes per second.
+H=7168 -- rmsnorm_quant (ROW) whose quantized activation feeds every K=7168
+consumer (N=4096/512/512/4096 plus N=12288 and N=96) in one grouped
+q8_gemv_shared_multi launch, then q8_quantize of a K=128 vector feeding
+q8_gemv N=4096 K=128. One step is those four launches; `value` is the step's
+algorithmic HBM bytes per second.
 Weights rotate over enough distinct copies (>= 1 GB) that no step finds its
 weights in the 256 MB Infinity Cache or the L2s. The steps are captured once
 in a HIP graph and replayed; inputs are resident in HBM before timing.
@@ -142,20 +143,38 @@ def time_each(D, fn, reps, warm=3):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def time_batch(D, fn, reps, warm=3):
+    """Mean device time per call of fn(i) over `reps` back-to-back calls, with one pair of
+    HIP events around the whole batch (no event between launches)."""
+    torch = D.torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2.4e9 * (1e-3 + 40e-6 * reps)))
+    a.record()
+    for i in range(reps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 # ---------------------------------------------------------------------------
 # Headline: decode projection set, H=7168
 # ---------------------------------------------------------------------------
 DEC_N = {"Wq": 4096, "Wk": 512, "Wv": 512, "Wg": 4096, "W12288": 12288, "W96": 96, "W128": 4096}
 
 
+DEC_GROUP = ("Wq", "Wk", "Wv", "Wg", "W12288", "W96")  # every consumer of the normed activation
+
+
 def decode_step_bytes():
     H = 7168
-    grouped = sum(gemv_bytes(DEC_N[n], H) for n in ("Wq", "Wk", "Wv", "Wg")) - 3 * (H + (H // 32) * 4)
+    grouped = sum(gemv_bytes(DEC_N[n], H) for n in DEC_GROUP) - (len(DEC_GROUP) - 1) * (H + (H // 32) * 4)
     parts = {
         "rmsnorm_quant_row": rms_bytes(1, H),
-        "q8_gemv_shared_multi": grouped,
-        "q8_gemv_12288x7168": gemv_bytes(12288, H),
-        "q8_gemv_96x7168": gemv_bytes(96, H),
+        "q8_gemv_shared_multi_x6": grouped,
         "q8_quantize_128": quant_bytes(1, 128),
         "q8_gemv_4096x128": gemv_bytes(4096, 128),
     }
@@ -184,13 +203,21 @@ def bench_decode(D, steps, warmup, log_reps):
         S = sets[c % ncopy]
         return [
             ("rmsnorm_quant_row", lambda: q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_ROW, y, aq, asd)),
-            ("q8_gemv_shared_multi", lambda: q8.q8_gemv_shared_multi(
-                [S["Wq"], S["Wk"], S["Wv"], S["Wg"]], aq, asd, [outs["Wq"], outs["Wk"], outs["Wv"], outs["Wg"]])),
-            ("q8_gemv_12288x7168", lambda: q8.q8_gemv(S["W12288"], aq, asd, outs["W12288"])),
-            ("q8_gemv_96x7168", lambda: q8.q8_gemv(S["W96"], aq, asd, outs["W96"])),
+            ("q8_gemv_shared_multi_x6", lambda: q8.q8_gemv_shared_multi(
+                [S[n] for n in DEC_GROUP], aq, asd, [outs[n] for n in DEC_GROUP])),
             ("q8_quantize_128", lambda: q8.q8_quantize(x128, q8.LAYOUT_ROW, bq, bsd)),
             ("q8_gemv_4096x128", lambda: q8.q8_gemv(S["W128"], bq, bsd, outs["W128"])),
         ]
+
+    def standalone(c):  # the same GEMVs as separate launches, for comparison
+        S = sets[c % ncopy]
+        return {
+            "q8_gemv_shared_multi_x4": (lambda: q8.q8_gemv_shared_multi(
+                [S[n] for n in DEC_GROUP[:4]], aq, asd, [outs[n] for n in DEC_GROUP[:4]]),
+                sum(gemv_bytes(DEC_N[n], H) for n in DEC_GROUP[:4]) - 3 * (H + (H // 32) * 4)),
+            "q8_gemv_12288x7168": (lambda: q8.q8_gemv(S["W12288"], aq, asd, outs["W12288"]), gemv_bytes(12288, H)),
+            "q8_gemv_96x7168": (lambda: q8.q8_gemv(S["W96"], aq, asd, outs["W96"]), gemv_bytes(96, H)),
+        }
 
     def step(c):
         for _, f in launches(c):
@@ -230,6 +257,16 @@ def bench_decode(D, steps, warmup, log_reps):
         gbs = parts[name] / (st["mean_us"] * 1e-6) / 1e9
         comp[name] = {**st, "bytes": parts[name], "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
                       "launches_per_step": 1}
+        tb = time_batch(D, lambda i, idx=idx: launches(i)[idx][1](), 4 * log_reps)
+        comp[name]["batch_mean_us"] = tb * 1e3
+        comp[name]["batch_GBps"] = parts[name] / (tb * 1e-3) / 1e9
+    for name in standalone(0):
+        t = time_each(D, lambda i, name=name: standalone(i)[name][0](), log_reps)
+        st = stats(t)
+        b = standalone(0)[name][1]
+        comp["separate_" + name] = {**st, "bytes": b, "GBps": b / (st["mean_us"] * 1e-6) / 1e9,
+                                    "frac_hbm": b / (st["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                    "launches_per_step": 0}
     del g
     return {"ms_per_step": ms / steps, "step_bytes": step_bytes, "value_GBps": step_bytes * steps / (ms * 1e-3) / 1e9,
             "copies": ncopy, "components": comp, "launches_per_step": len(parts)}
@@ -381,7 +418,7 @@ def cpu_baseline(budget_s=10.0, max_steps=100000):
     def step():
         y = oracle.rmsnorm_f64(x, w, EPS).astype(np.float32)
         aq, ad, _ = oracle.quantize(y)
-        for n in ("Wq", "Wk", "Wv", "Wg", "W12288", "W96"):
+        for n in DEC_GROUP:
             oracle.gemv(Wq[n][0], Wq[n][1], aq[0], ad[0])
         bq, bd, _ = oracle.quantize(x128)
         oracle.gemv(Wq["W128"][0], Wq["W128"][1], bq[0], bd[0])
@@ -448,7 +485,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall-clock budget of the oracle CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     ensure_built()
@@ -476,12 +513,15 @@ def main():
             log(f"[{name}] running")
             per[name] = fn(D, args.reps)
             torch.cuda.empty_cache()
-    dom_name = "q8_gemv_12288x7168"
+    dom_name = "q8_gemv_shared_multi_x6"
     dom = dec["components"][dom_name]
-    achieved = dom["bytes"] / (dom["mean_us"] * 1e-6) / 1e9
+    # average launch duration: HIP events around a batch of back-to-back launches on the
+    # launch stream (weights rotate over cold copies); per-launch event pairs are in components
+    achieved = dom["bytes"] / (dom["batch_mean_us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(dom_name),
-                "algorithmic_bytes": dom["bytes"], "mean_launch_us": dom["mean_us"]}
+                "algorithmic_bytes": dom["bytes"], "mean_launch_us": dom["batch_mean_us"],
+                "launches_timed": 4 * args.reps}
     cpu = None
     if not args.no_cpu:
         log("[cpu] timing the oracle")
@@ -491,8 +531,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": dec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": "decode_h7168", "batch": 1, "hidden": 7168,
-                   "gemvs": "rmsnorm_quant ROW -> shared_multi N=4096/512/512/4096; N=12288, N=96 (K=7168); "
-                            "q8_quantize K=128 -> N=4096 K=128",
+                   "gemvs": "rmsnorm_quant ROW -> one grouped q8_gemv_shared_multi over N=4096/512/512/4096/"
+                            "12288/96 (K=7168); q8_quantize K=128 -> q8_gemv N=4096 K=128",
                    "launches_per_step": dec["launches_per_step"], "weight_copies": dec["copies"],
                    "timing": "HIP graph of all timed steps, HIP events around the replay"},
         "roofline": roofline,

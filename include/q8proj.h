@@ -133,8 +133,9 @@ int q8_gemv(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, float
 
 /*
  * Several GEMVs that read the same activation, in one launch ([P1] s2.5,
- * s6: one activation feeding q/k/v/g, generalised to unequal N).
- * m: 1..4. W: host array of m host pointers, all with the same k. y: host
+ * s6: one activation feeding q/k/v/g, and the "more general grouped kernel"
+ * for consumers of one activation at different N).
+ * m: 1..8. W: host array of m host pointers, all with the same k. y: host
  * array of m device pointers, y[i] of length W[i]->n. Each y[i] is
  * bit-identical to q8_gemv(W[i], ...).
  */

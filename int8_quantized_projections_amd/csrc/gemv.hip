@@ -26,7 +26,7 @@ using namespace q8;
 
 namespace {
 
-constexpr int kMaxMats = 4;
+constexpr int kMaxMats = 8;
 constexpr int kWavesPerWg = 4;
 constexpr int kMaxWaves = 256 * 16;  // persistent grid cap: 256 CUs x 16 resident waves
 
@@ -67,8 +67,10 @@ __device__ __forceinline__ int dot32(const uint4& w0, const uint4& w1, const uin
 
 // W: lanes per row. NBL: blocks per lane held in registers per K chunk
 // (a chunk is W*NBL blocks; K wider than one chunk reloads the activation
-// chunk per row group). R: rows per lane group per iteration.
-template <int W, int NBL, int R>
+// chunk per row group). R: rows per lane group per iteration. MULTI: rows
+// are the concatenation of several matrices (the grouped launch); the
+// per-row arithmetic is the same code either way.
+template <int W, int NBL, int R, bool MULTI>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __restrict__ aq,
                                               const uint32_t* __restrict__ asd, int K, int nb, int64_t groups) {
     constexpr int G = kWave / W;  // row slots per wave
@@ -105,11 +107,20 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __res
         for (int r = 0; r < R; ++r) {
             const int64_t row = gi * (G * R) + r * G + slot;
             valid[r] = row < args.total;
-            const int mi = (row >= args.off[1]) + (row >= args.off[2]) + (row >= args.off[3]);
-            const int8_t* q = mi == 0 ? args.wq[0] : mi == 1 ? args.wq[1] : mi == 2 ? args.wq[2] : args.wq[3];
-            const uint16_t* d = mi == 0 ? args.wd[0] : mi == 1 ? args.wd[1] : mi == 2 ? args.wd[2] : args.wd[3];
-            float* yy = mi == 0 ? args.y[0] : mi == 1 ? args.y[1] : mi == 2 ? args.y[2] : args.y[3];
-            const int64_t o = mi == 0 ? args.off[0] : mi == 1 ? args.off[1] : mi == 2 ? args.off[2] : args.off[3];
+            const int8_t* q = args.wq[0];
+            const uint16_t* d = args.wd[0];
+            float* yy = args.y[0];
+            int64_t o = 0;
+            if constexpr (MULTI) {  // the member matrix this row belongs to (rows are concatenated)
+#pragma unroll
+                for (int i = 1; i < kMaxMats; ++i) {
+                    const bool in = row >= args.off[i];
+                    q = in ? args.wq[i] : q;
+                    d = in ? args.wd[i] : d;
+                    yy = in ? args.y[i] : yy;
+                    o = in ? args.off[i] : o;
+                }
+            }
             const int64_t local = valid[r] ? row - o : 0;
             wrow[r] = valid[r] ? q + local * K : args.safe_q;
             drow[r] = valid[r] ? d + local * nb : args.safe_d;
@@ -190,34 +201,43 @@ Plan make_plan(int64_t total, int nb, int force_rows) {
     return p;
 }
 
-template <int W, int NBL>
+template <int W, int NBL, bool MULTI>
 void launch_r(const Plan& p, dim3 grid, hipStream_t s, const GemvArgs& a, const int8_t* aq, const uint32_t* asd,
               int K, int nb) {
     if (p.rows == 4)
-        hipLaunchKernelGGL((k_gemv<W, NBL, 4>), grid, dim3(256), 0, s, a, aq, asd, K, nb, p.groups);
+        hipLaunchKernelGGL((k_gemv<W, NBL, 4, MULTI>), grid, dim3(256), 0, s, a, aq, asd, K, nb, p.groups);
     else if (p.rows == 2)
-        hipLaunchKernelGGL((k_gemv<W, NBL, 2>), grid, dim3(256), 0, s, a, aq, asd, K, nb, p.groups);
+        hipLaunchKernelGGL((k_gemv<W, NBL, 2, MULTI>), grid, dim3(256), 0, s, a, aq, asd, K, nb, p.groups);
     else
-        hipLaunchKernelGGL((k_gemv<W, NBL, 1>), grid, dim3(256), 0, s, a, aq, asd, K, nb, p.groups);
+        hipLaunchKernelGGL((k_gemv<W, NBL, 1, MULTI>), grid, dim3(256), 0, s, a, aq, asd, K, nb, p.groups);
 }
 
-void launch(const Plan& p, hipStream_t s, const GemvArgs& a, const int8_t* aq, const uint32_t* asd, int K, int nb) {
+template <bool MULTI>
+void launch_m(const Plan& p, hipStream_t s, const GemvArgs& a, const int8_t* aq, const uint32_t* asd, int K, int nb) {
     const dim3 grid((unsigned)p.workgroups);
     switch (p.lanes) {
-        case 1: launch_r<1, 1>(p, grid, s, a, aq, asd, K, nb); break;
-        case 2: launch_r<2, 1>(p, grid, s, a, aq, asd, K, nb); break;
-        case 4: launch_r<4, 1>(p, grid, s, a, aq, asd, K, nb); break;
-        case 8: launch_r<8, 1>(p, grid, s, a, aq, asd, K, nb); break;
-        case 16: launch_r<16, 1>(p, grid, s, a, aq, asd, K, nb); break;
-        case 32: launch_r<32, 1>(p, grid, s, a, aq, asd, K, nb); break;
+        case 1: launch_r<1, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
+        case 2: launch_r<2, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
+        case 4: launch_r<4, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
+        case 8: launch_r<8, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
+        case 16: launch_r<16, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
+        case 32: launch_r<32, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
         default:
             if (p.nbl == 1)
-                launch_r<64, 1>(p, grid, s, a, aq, asd, K, nb);
+                launch_r<64, 1, MULTI>(p, grid, s, a, aq, asd, K, nb);
             else if (p.nbl == 2)
-                launch_r<64, 2>(p, grid, s, a, aq, asd, K, nb);
+                launch_r<64, 2, MULTI>(p, grid, s, a, aq, asd, K, nb);
             else
-                launch_r<64, 4>(p, grid, s, a, aq, asd, K, nb);
+                launch_r<64, 4, MULTI>(p, grid, s, a, aq, asd, K, nb);
     }
+}
+
+void launch(const Plan& p, bool multi, hipStream_t s, const GemvArgs& a, const int8_t* aq, const uint32_t* asd, int K,
+            int nb) {
+    if (multi)
+        launch_m<true>(p, s, a, aq, asd, K, nb);
+    else
+        launch_m<false>(p, s, a, aq, asd, K, nb);
 }
 
 int check_weights(const q8_weights* w) {
@@ -282,7 +302,19 @@ int q8_gemv_shared_multi_ex(int m, const q8_weights* const* W, const int8_t* a_q
     if (total == 0) return Q8_OK;
     const int nb = (int)(K / kQK);
     const Plan p = make_plan(total, nb, rows_per_wave);
-    launch(p, (hipStream_t)stream, a, a_qs, a_sd, (int)K, nb);
+    // one non-empty member: the plain kernel, reading member 0's pointers
+    int nonempty = 0, first = 0;
+    for (int i = m - 1; i >= 0; --i)
+        if (W[i]->n > 0) {
+            ++nonempty;
+            first = i;
+        }
+    if (nonempty == 1) {
+        a.wq[0] = a.wq[first];
+        a.wd[0] = a.wd[first];
+        a.y[0] = a.y[first];
+    }
+    launch(p, nonempty > 1, (hipStream_t)stream, a, a_qs, a_sd, (int)K, nb);
     return q8h::launch_status();
 }
 

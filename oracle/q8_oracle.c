@@ -136,8 +136,9 @@ void q8o_pack_sd(const uint16_t* d16, const int16_t* ssum, int64_t n, uint32_t* 
 /* ------------------------------------------------------------------------
  * PLANE64 layout: tokens grouped 64 at a time ([P2] s2.1: the token dimension
  * is grouped in 64s and padded), one 2048-byte qs tile and 64 scale words per
- * (group, 32-element chunk). The byte placement inside a tile is this
- * build's own (the pages' XOR formula targets another GPU's memory banks):
+ * (group, 32-element chunk). The byte placement inside a tile is the one
+ * the HIP library documents for its plane (the pages' XOR formula targets
+ * another GPU's memory banks):
  *   token r = t mod 64 owns bytes [32r, 32r + 32) of the tile;
  *   its 16-byte half h (elements 16h..16h+15) sits at half position
  *   h ^ (((r >> 2) ^ (r >> 3)) & 1).

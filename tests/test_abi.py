@@ -102,7 +102,7 @@ def test_gemv_and_gemm_reject_before_launch(L):
     ys = (ctypes.c_void_p * 2)(f, f)
     assert L.q8_gemv_shared_multi(2, ws, f, f, ys, None) == Q8_ESHAPE
     assert L.q8_gemv_shared_multi(0, ws, f, f, ys, None) == Q8_EINVAL
-    assert L.q8_gemv_shared_multi(5, ws, f, f, ys, None) == Q8_EINVAL
+    assert L.q8_gemv_shared_multi(9, ws, f, f, ys, None) == Q8_EINVAL
     assert L.q8_gemv_shared_multi_ex(1, ws, f, f, ys, 3, None) == Q8_EINVAL
     # gemm
     assert L.q8_gemm(ctypes.byref(w), f, f, 5, f, 4, None) == Q8_ESHAPE  # ldc < N

@@ -93,6 +93,28 @@ def test_shared_multi_unequal_n_bit_identical_to_separate():
         assert_norm(to_np(y), ref, norm, 1e-5, "shared_multi")
 
 
+def test_shared_multi_eight_members_mixed_sizes():
+    K = 2080  # 65 blocks
+    x = synth.normal((1, K), stream=4700)
+    aq, asd, qo, do, _ = row_act(x)
+    sizes = [1, 96, 0, 3, 1025, 4, 64, 130]
+    Ws, refs = [], []
+    for i, n in enumerate(sizes):
+        W, wq, wd = weights(synth.normal((max(n, 1), K), stream=4710 + i, std=0.02))
+        if n == 0:
+            W = W.rows(0, 0)
+        Ws.append(W)
+        refs.append(oracle.gemv(wq, wd, qo[0], do[0]) if n else None)
+    ys = [poisoned(max(W.n, 1), torch.float32, 0xFF)[: W.n] for W in Ws]
+    q8lib.q8_gemv_shared_multi(Ws, aq, asd, ys)
+    sep = [run_gemv(W, aq, asd) if W.n else None for W in Ws]
+    torch.cuda.synchronize()
+    for y, s, r in zip(ys, sep, refs):
+        if r is not None:
+            assert_norm(to_np(y), r[0], r[1], 1e-5, "member")
+            assert torch.equal(y, s)
+
+
 def test_shared_multi_small_and_empty_members():
     K = 640
     x = synth.normal((1, K), stream=4400)
