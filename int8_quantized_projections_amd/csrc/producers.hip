@@ -35,38 +35,63 @@ __device__ __forceinline__ void store_quant(const Quant8& r, int64_t t, int c, i
 }
 
 // ---------------------------------------------------------------------------
-// Element-wise producers (quantize of x, or swiglu then quantize).
-// Grid: x = row (token, padded to 64 for PLANE64), y = chunk of units. A unit
-// is 8 consecutive blocks = 256 floats = one float4 per lane. Each wave does
-// UNR units, issuing all loads before any math.
+// Element-wise producers (quantize of x, or swiglu then quantize). A unit is
+// 8 consecutive blocks of one row = 256 floats = one float4 per lane. Each
+// wave does kUnr units, issuing all loads before any math; rows are padded to
+// 64 for PLANE64.
 // ---------------------------------------------------------------------------
 constexpr int kUnr = 4;
 constexpr int kWavesPerWg = 4;
 
 template <int D, bool SWIGLU>
 __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a, const float* __restrict__ b,
-                                                     float* __restrict__ y, int64_t rows, int K, int nb,
-                                                     int8_t* __restrict__ qs, uint32_t* __restrict__ sd) {
-    const int64_t t = blockIdx.x;
+                                                     float* __restrict__ y, int64_t rows, int K, int nb, int upr,
+                                                     int64_t units, int8_t* __restrict__ qs, uint32_t* __restrict__ sd) {
+    // The work is a flat list of (row, unit) pairs, upr units per row (a unit
+    // is 8 blocks = 256 values; the last unit of a row may be partial). ROW and
+    // f32-only outputs take it row-major. PLANE64 takes it as (64-row group,
+    // unit column, row in the group), so consecutive waves finish whole 2048-byte
+    // tiles together. Wave w of logical workgroup L takes kUnr consecutive
+    // pairs; logical workgroups are spread over the XCDs in contiguous ranges,
+    // so each tile is assembled in one L2.
+    const int64_t L = xcd_contiguous(blockIdx.x, gridDim.x);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int unit0 = (blockIdx.y * kWavesPerWg + wave) * kUnr;
-    const bool live = t < rows;
     const int sub = lane & 7;
+    const int64_t first = (L * kWavesPerWg + wave) * kUnr;
     float4 v[kUnr], w[kUnr];
     int blk[kUnr];
+    int64_t trow[kUnr];
+    bool live[kUnr];
     // Unconditional loads from clamped, always-valid addresses (a load inside a
     // divergent branch serialises the stream); padded rows read row 0 and are
-    // zeroed afterwards.
-    const int64_t trow = live ? t : 0;
+    // zeroed at use.
 #pragma unroll
     for (int u = 0; u < kUnr; ++u) {
-        blk[u] = (unit0 + u) * 8 + (lane >> 3);
+        const int64_t un = first + u < units ? first + u : units - 1;  // wave-uniform
+        int64_t col;
+        if constexpr (D == kDstPlane) {
+            const int64_t gj = un / kGroup;  // group * upr + unit column
+            trow[u] = (gj / upr) * kGroup + un % kGroup;
+            col = gj % upr;
+        } else {
+            trow[u] = un / upr;
+            col = un % upr;
+        }
+        blk[u] = (int)col * 8 + (lane >> 3);
+        if (first + u >= units) blk[u] = nb;  // past the end: no output
+        live[u] = trow[u] < rows;
         const int bc = blk[u] < nb ? blk[u] : nb - 1;
-        const int64_t off = trow * K + (int64_t)bc * kQK + sub * 4;
+        const int64_t off = (live[u] ? trow[u] : 0) * K + (int64_t)bc * kQK + sub * 4;
         v[u] = *reinterpret_cast<const float4*>(a + off);
         if constexpr (SWIGLU) w[u] = *reinterpret_cast<const float4*>(b + off);
     }
-
+    // PLANE64: this workgroup covers rows 16k..16k+15 of one 64-row group at one
+    // 8-chunk column, i.e. a 512-byte slice of each of 8 tiles. The quantized
+    // bytes are gathered in LDS and written as whole slices (16 bytes per lane).
+    constexpr int kSlice = kWavesPerWg * kUnr;  // rows per workgroup (16)
+    constexpr int kCs = kSlice * 8 + 8;  // words per chunk slice, padded against bank conflicts
+    __shared__ __attribute__((aligned(16))) uint32_t pq[D == kDstPlane ? 8 * kCs : 1];
+    __shared__ uint32_t psd[D == kDstPlane ? 8 * kSlice : 1];
 #pragma unroll
     for (int u = 0; u < kUnr; ++u) {
         if (blk[u] >= nb) continue;  // whole 8-lane groups drop out together
@@ -78,13 +103,42 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
             o.y = v[u].y * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].y)) * w[u].y;
             o.z = v[u].z * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].z)) * w[u].z;
             o.w = v[u].w * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].w)) * w[u].w;
-            if (live) *reinterpret_cast<float4*>(y + t * K + (int64_t)blk[u] * kQK + sub * 4) = o;
+            if (live[u]) *reinterpret_cast<float4*>(y + trow[u] * K + (int64_t)blk[u] * kQK + sub * 4) = o;
             v[u] = o;
         }
         if constexpr (D != kDstNone) {
             // padded rows (which loaded row 0) quantize a zero block: all bytes zero
-            const Quant8 r = quantize_block8(live ? v[u] : make_float4(0.f, 0.f, 0.f, 0.f));
-            store_quant<D>(r, t, blk[u], sub * 4, K, nb, qs, sd);
+            const Quant8 r = quantize_block8(live[u] ? v[u] : make_float4(0.f, 0.f, 0.f, 0.f));
+            if constexpr (D == kDstPlane) {
+                const int rs = wave * kUnr + u;  // row in the slice
+                const int rt = (int)(trow[u] & 63);  // row in the tile (selects the half swizzle)
+                const int e = sub * 4;
+                const int h = ((e >> 4) ^ (rt >> 2) ^ (rt >> 3)) & 1;
+                const int cl = lane >> 3;  // chunk in the column
+                pq[cl * kCs + rs * 8 + h * 4 + ((e & 15) >> 2)] = r.qs4;
+                if (sub == 0) psd[cl * kSlice + rs] = r.sd;
+            } else {
+                store_quant<D>(r, trow[u], blk[u], sub * 4, K, nb, qs, sd);
+            }
+        }
+    }
+    if constexpr (D == kDstPlane) {
+        __syncthreads();
+        const int64_t g = trow[0] >> 6;  // same group and column for the whole workgroup
+        const int r0 = (int)(trow[0] & 63) - wave * kUnr;  // first row of the slice
+        // qs: 8 chunks x 512 bytes; thread i writes 16 bytes of chunk i / 32
+        const int tid = threadIdx.x;
+        const int cl = tid >> 5;
+        const int64_t first_u = (L * kWavesPerWg) * kUnr;
+        const int64_t col = (first_u / kGroup) % upr;
+        const int c = (int)col * 8 + cl;
+        if (c < nb) {
+            const uint4 v4 = *reinterpret_cast<const uint4*>(&pq[cl * kCs + (tid & 31) * 4]);
+            *reinterpret_cast<uint4*>(qs + (g * nb + c) * kTileBytes + r0 * 32 + (tid & 31) * 16) = v4;
+        }
+        if (tid < 8 * kSlice) {
+            const int c2 = (int)col * 8 + tid / kSlice;
+            if (c2 < nb) sd[(g * nb + c2) * kGroup + r0 + tid % kSlice] = psd[tid];
         }
     }
 }
@@ -107,7 +161,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, co
     constexpr int kStride = kWave * WPR;  // float4 stride between a lane's elements
     __shared__ float part[kWavesPerWg];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * kRowsPerWg + wave / WPR;
+    const int64_t t = xcd_contiguous(blockIdx.x, gridDim.x) * kRowsPerWg + wave / WPR;
     const int li = (wave % WPR) * kWave + lane;  // lane index inside the row
     const bool live = t < rows;
     const bool inrow = t < tpad;  // uniform per wave
@@ -258,15 +312,20 @@ int launch_elementwise(const float* a, const float* b, float* y, int64_t rows, i
     const int nb = (int)(k / kQK);
     const int64_t tpad = (qs == nullptr) ? rows : padded_rows(rows, layout);
     if (tpad == 0) return Q8_OK;
-    const int units = (nb + 7) / 8;
-    const dim3 grid((unsigned)tpad, (unsigned)q8h::ceil_div(units, kWavesPerWg * kUnr));
+    const int upr = (nb + 7) / 8;  // units per row
+    const int64_t units = tpad * upr;
+    const int64_t wgs = q8h::ceil_div(units, kWavesPerWg * kUnr);
+    if (wgs > INT32_MAX) return Q8_ESHAPE;
+    const dim3 grid((unsigned)wgs);
     if (qs == nullptr) {
-        hipLaunchKernelGGL((k_elementwise<kDstNone, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, qs, sd);
+        hipLaunchKernelGGL((k_elementwise<kDstNone, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, upr,
+                           units, qs, sd);
     } else if (layout == Q8_LAYOUT_ROW) {
-        hipLaunchKernelGGL((k_elementwise<kDstRow, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, qs, sd);
+        hipLaunchKernelGGL((k_elementwise<kDstRow, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, upr,
+                           units, qs, sd);
     } else {
-        hipLaunchKernelGGL((k_elementwise<kDstPlane, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, qs,
-                           sd);
+        hipLaunchKernelGGL((k_elementwise<kDstPlane, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, upr,
+                           units, qs, sd);
     }
     return q8h::launch_status();
 }
@@ -304,9 +363,10 @@ int rms_nv(int64_t k, int wpr) {
     return 0;
 }
 
-// Waves per row: spread a row over 4 waves when there are too few rows to
-// fill the GPU with one wave per row.
-int rms_wpr(int64_t rows) { return rows < 1024 ? 4 : 1; }
+// Waves per row: 4 when there are few rows (a decode row spreads over 256
+// lanes), else 2 (half the row per wave keeps the kernel near 100 VGPRs, so
+// enough waves are resident to stream).
+int rms_wpr(int64_t rows) { return rows < 1024 ? 4 : 2; }
 
 template <int D>
 void dispatch_rms(hipStream_t s, const float* x, const float* w, float eps, float* y, int64_t rows, int64_t tpad,
@@ -317,7 +377,7 @@ void dispatch_rms(hipStream_t s, const float* x, const float* w, float eps, floa
     if (wpr == 4)
         launch_rms<D, 4>(nv, grid, s, x, w, eps, y, rows, tpad, k, nb, qs, sd);
     else
-        launch_rms<D, 1>(nv, grid, s, x, w, eps, y, rows, tpad, k, nb, qs, sd);
+        launch_rms<D, 2>(nv, grid, s, x, w, eps, y, rows, tpad, k, nb, qs, sd);
 }
 
 }  // namespace

@@ -116,6 +116,15 @@ __device__ __forceinline__ Quant8 quantize_block8(float4 v) {
     return res;
 }
 
+// Workgroups are dealt to the 8 XCDs in turn (workgroup p runs on XCD p % 8).
+// Remap a linear workgroup index so that each XCD gets one contiguous range
+// of logical indices: neighbouring rows then share an XCD, so the 64 rows of
+// a plane tile are assembled in one L2 instead of eight.
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t p, int64_t count) {
+    if (count % 8 != 0) return p;
+    return (p % 8) * (count / 8) + p / 8;
+}
+
 // PLANE64 addressing. Byte offset, inside the qs plane, of the 4-byte group
 // holding elements e..e+3 (e % 4 == 0) of chunk c of token t.
 __device__ __forceinline__ int64_t plane_qs_off(int64_t t, int c, int e, int nchunk) {
