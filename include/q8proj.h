@@ -161,7 +161,7 @@ int q8_gemv_plan(int64_t total_rows, int64_t k, int rows_per_wave, int* lanes_pe
  * plane in bulk; [P3] s2-s3): C[t][n] = sum_b f16(da[t,b]) * f16(dw[n,b]) * isum[t,n,b].
  * a_qs, a_sd: a PLANE64 activation of T tokens and width W->k.
  * C: [T][ldc] f32, row-major, ldc >= N; only columns n < N of rows t < T are
- * written.
+ * written. K <= 2^24 (Q8_ESHAPE otherwise).
  */
 int q8_gemm(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t, float* c, int64_t ldc,
             void* stream);

@@ -21,18 +21,18 @@
 //    and a DPP row_newbcast:r broadcast hands it to all 16 lanes.
 //  - Workgroup tile: 64 tokens (one plane group) x 128 weight rows, 4 waves;
 //    wave w owns weight rows 32w..32w+31 and both 32-token halves (two MFMA
-//    tiles per K block). The A plane tile (8 chunks = 16 KB) is copied
-//    verbatim into LDS; weight fragments are wave-private and are loaded
-//    straight into VGPRs.
+//    tiles per K block). Both operands and their scales go global -> LDS with
+//    the direct copy, each copy instruction reading whole cache lines (8
+//    lanes per 128-byte weight row): per-lane row-strided loads cost one L1
+//    tag lookup per lane and made the vector-memory path the bottleneck.
 #include "q8_common.h"
-
-#include <type_traits>
 
 using namespace q8;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -54,6 +54,16 @@ constexpr float kBiasF = 12582912.0f;  // 1.5 * 2^23
         : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)                                            \
         : "v"(sv), "v"(u0), "v"(u1), "v"(u2), "v"(u3))
 
+// The same without the leading s_nop, for the blocks after the first: s is
+// not written between them.
+#define Q8_FMAC_DPP4_NONOP(a0, a1, a2, a3, sv, u0, u1, u2, u3, R0, R1, R2, R3)             \
+    asm("v_fmac_f32_dpp %0, %4, %5 row_newbcast:" #R0 " row_mask:0xf bank_mask:0xf\n\t"    \
+        "v_fmac_f32_dpp %1, %4, %6 row_newbcast:" #R1 " row_mask:0xf bank_mask:0xf\n\t"    \
+        "v_fmac_f32_dpp %2, %4, %7 row_newbcast:" #R2 " row_mask:0xf bank_mask:0xf\n\t"    \
+        "v_fmac_f32_dpp %3, %4, %8 row_newbcast:" #R3 " row_mask:0xf bank_mask:0xf"         \
+        : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)                                            \
+        : "v"(sv), "v"(u0), "v"(u1), "v"(u2), "v"(u3))
+
 // One 32x32 tile's epilogue for one K block. d is the MFMA result reinterpreted
 // as f32 as a whole vector (in this compiler, bit-casting a single
 // ext_vector element yields element 0).
@@ -62,65 +72,114 @@ __device__ __forceinline__ void epilogue(float (&acc)[16], const v16f& d, float 
 #pragma unroll
     for (int r = 0; r < 16; ++r) u[r] = fmaf(d[r], dw, nbias);  // = round(isum * dw)
     Q8_FMAC_DPP4(acc[0], acc[1], acc[2], acc[3], s, u[0], u[1], u[2], u[3], 0, 1, 2, 3);
-    Q8_FMAC_DPP4(acc[4], acc[5], acc[6], acc[7], s, u[4], u[5], u[6], u[7], 4, 5, 6, 7);
-    Q8_FMAC_DPP4(acc[8], acc[9], acc[10], acc[11], s, u[8], u[9], u[10], u[11], 8, 9, 10, 11);
-    Q8_FMAC_DPP4(acc[12], acc[13], acc[14], acc[15], s, u[12], u[13], u[14], u[15], 12, 13, 14, 15);
+    Q8_FMAC_DPP4_NONOP(acc[4], acc[5], acc[6], acc[7], s, u[4], u[5], u[6], u[7], 4, 5, 6, 7);
+    Q8_FMAC_DPP4_NONOP(acc[8], acc[9], acc[10], acc[11], s, u[8], u[9], u[10], u[11], 8, 9, 10, 11);
+    Q8_FMAC_DPP4_NONOP(acc[12], acc[13], acc[14], acc[15], s, u[12], u[13], u[14], u[15], 12, 13, 14, 15);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Global -> LDS direct copy of 16 (or 4) bytes per lane: lane i's bytes land at
-// lds + 16*i (4*i). `lds` must be the same for the whole wave.
-__device__ __forceinline__ void lds_copy16(const void* g, void* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_copy4(const void* g, void* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, 0);
-}
-
-// Logical tile of physical workgroup p: workgroups are dealt to the 8 XCDs in
-// turn, so give each XCD a contiguous range of logical tiles (neighbouring
-// tiles share A or B strips in that XCD's L2).
-__device__ __forceinline__ int64_t xcd_tile(int64_t p, int64_t tiles) {
-    if (tiles % 8 != 0) return p;
-    return (p % 8) * (tiles / 8) + p / 8;
+// Buffer resource over `bytes` bytes from `base` (raw, stride 0; the third
+// word's data format must be non-zero on gfx9). Reads past `bytes` return
+// zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int nrec = (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nrec, 0x00020000);
 }
 
-__global__ __launch_bounds__(256) void k_gemm(const int8_t* __restrict__ aq, const uint32_t* __restrict__ asd,
-                                              const int8_t* __restrict__ wq, const uint16_t* __restrict__ wd,
-                                              float* __restrict__ C, int64_t T, int64_t N, int K, int nb, int64_t ldc,
-                                              int n_tiles, int64_t tiles) {
-    // Double-buffered stage of the A plane (kKT chunks of one 64-token group,
-    // copied verbatim) and of its raw scale words.
+// Buffer -> LDS direct copy of 16 (or 4) bytes per lane from byte offset
+// voff + soff of the resource: lane i's bytes land at lds + 16*i (4*i). `lds`
+// and `soff` must be the same for the whole wave.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
+}
+
+// Wait until every global -> LDS copy this wave issued has landed
+// (s_waitcnt vmcnt(0); the expcnt and lgkmcnt fields are left at their maxima).
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Tile order: the n-tiles are cut into panels of kPanel; a panel's tiles are
+// taken token group by token group. With each XCD given a contiguous range of
+// this order, the ~96 tiles resident on one XCD span about 8 n-tiles x 12
+// token groups, so the weight and activation strips they stream are shared in
+// that XCD's L2 (in group-major order every XCD would stream the whole weight
+// matrix, and a wide LM head would be read from HBM eight times).
+constexpr int kPanel = 8;
+
+__device__ __forceinline__ void tile_of(int64_t p, int64_t tiles, int n_tiles, int& nt, int64_t& g) {
+    const int64_t L = xcd_contiguous(p, tiles);
+    const int64_t ng = tiles / n_tiles;
+    const int full = (n_tiles / kPanel) * kPanel;  // n-tiles in whole panels
+    if (L < (int64_t)full * ng) {
+        const int64_t r = L % ((int64_t)kPanel * ng);
+        g = r / kPanel;
+        nt = (int)(L / ((int64_t)kPanel * ng)) * kPanel + (int)(r % kPanel);
+    } else {
+        const int64_t r = L - (int64_t)full * ng;
+        const int rem = n_tiles - full;
+        g = r / rem;
+        nt = full + (int)(r % rem);
+    }
+}
+
+// Weight tile in LDS: 128 rows of 128 bytes (4 blocks); the 16-byte piece p
+// (block p/2, half p%2) of tile row r sits at slot 8r + (p ^ wsw(r)). The copy
+// reads each row's 128 bytes with 8 consecutive lanes (whole cache lines), and
+// the fragment read (32 consecutive rows, one piece) touches every bank group
+// once per 8 or 16 lanes.
+__device__ __forceinline__ int wsw(int r) { return (r ^ (r >> 3)) & 7; }
+
+// DWL: the weight scales of a stage are copied into LDS with 4-byte copies of
+// block pairs, which needs K/32 even (4-byte aligned pairs); otherwise every
+// lane loads its own row's scales into registers one stage ahead.
+template <bool DWL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm(
+    const int8_t* __restrict__ aq, const uint32_t* __restrict__ asd, const int8_t* __restrict__ wq,
+    const uint16_t* __restrict__ wd, float* __restrict__ C, int64_t T, int64_t N, int K, int nb, int64_t ldc,
+    int n_tiles, int64_t tiles) {
+    // Double-buffered stage: kKT chunks of one 64-token group of the A plane
+    // (verbatim) with their scale words, and kKT blocks of the 128 weight rows
+    // (swizzled as above) with their scales.
     __shared__ __attribute__((aligned(16))) int8_t lds_a[2][kKT * kTileBytes];
+    __shared__ __attribute__((aligned(16))) int8_t lds_b[2][kBN * kKT * kQK];
     __shared__ __attribute__((aligned(16))) uint32_t lds_s[2][kKT * kGroup];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_w[2][DWL ? kBN * kKT / 2 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t tile = xcd_tile(blockIdx.x, tiles);
-    const int nt = (int)(tile % n_tiles);
-    const int64_t g = tile / n_tiles;
-    const int64_t nrow = (int64_t)nt * kBN + wave * 32 + (lane & 31);
+    int nt;
+    int64_t g;
+    tile_of(blockIdx.x, tiles, n_tiles, nt, g);
+    const int64_t n0 = (int64_t)nt * kBN;
+    const int brow = wave * 32 + (lane & 31);  // this lane's weight row in the tile
+    const int64_t nrow = n0 + brow;            // and its output column
     const bool nvalid = nrow < N;
     const int khalf = lane >> 5;
-    const int8_t* wrow = wq + (nvalid ? nrow : 0) * (int64_t)K + 16 * khalf;
-    const uint16_t* drow = wd + (nvalid ? nrow : 0) * (int64_t)nb;
 
     // Output register r of lane l covers tile row 8(r/4) + 4(l/32) + r%4; the
     // lane that feeds register r's broadcast in row-group q is 16q + r.
     const int rr = lane & 15, qq = lane >> 4;
     const int srow = 8 * (rr >> 2) + 4 * (qq >> 1) + (rr & 3);
-    // LDS byte offsets of this lane's A fragments (token 32h + lane%32, half khalf).
+    // LDS byte offsets of this lane's A fragments (token 32h + lane%32, half khalf)
+    // and of its B fragment of block 0 (the XOR with wsw is linear in the block,
+    // so block kb is at boff ^ (32 * kb)).
     int aoff[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int i = 32 * h + (lane & 31);
         aoff[h] = i * 32 + (((khalf ^ (i >> 2) ^ (i >> 3)) & 1) * 16);
     }
+    const int boff = brow * 128 + 16 * (khalf ^ wsw(brow));
 
     v16i bias;
 #pragma unroll
     for (int i = 0; i < 16; ++i) bias[i] = kBias;
+    // Opaque to the optimiser: held in 16 VGPRs for the whole kernel instead of
+    // being re-created from scalar registers before the MFMAs of every stage.
+    asm volatile("" : "+v"(bias));
     float acc[2][16];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -131,101 +190,155 @@ __global__ __launch_bounds__(256) void k_gemm(const int8_t* __restrict__ aq, con
     const uint32_t* splane = asd + g * (int64_t)nb * kGroup;
     const int nst = (nb + kKT - 1) / kKT;
 
-    // Issue the copies of stage st into LDS buffer b. Each wave copies whole
-    // 1 KB (A) or 256 B (scales) pieces, so the chunk a piece belongs to is
-    // wave-uniform; chunks past K read a clamped (valid) address, never used.
-    auto stage_a = [&](int st, int b) {
+    // Issue the copies of stage st into LDS buffer b. Every copy instruction
+    // fills one contiguous piece of LDS (1 KB, or 256 B). Each source is a
+    // buffer resource over this workgroup's part of an operand; in a full stage
+    // the byte offset is a per-lane offset fixed for the whole kernel plus a
+    // wave-uniform stage offset, so the copies cost no vector ALU work. A tail
+    // stage clamps every lane's block index to a valid block instead (those
+    // blocks are never used).
+    const __amdgpu_buffer_rsrc_t r_a = make_rsrc(plane, (int64_t)nb * kTileBytes);
+    const __amdgpu_buffer_rsrc_t r_s = make_rsrc(splane, (int64_t)nb * kGroup * 4);
+    const __amdgpu_buffer_rsrc_t r_b = make_rsrc(wq + n0 * (int64_t)K, (N - n0) * (int64_t)K);
+    const __amdgpu_buffer_rsrc_t r_w = make_rsrc(wd + n0 * (int64_t)nb, (N - n0) * (int64_t)nb * 2);
+    const uint32_t aoffs = (uint32_t)(wave * 1024 + lane * 16);  // + 4096 * it
+    const uint32_t soffs = (uint32_t)(wave * kGroup + lane) * 4;
+    uint32_t boffs[4];  // this lane's copy `it`: byte offset from the tile's first row, block 0
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int r = 32 * wave + 8 * it + (lane >> 3);
+        const int p = (lane & 7) ^ wsw(r);
+        boffs[it] = (uint32_t)((min(n0 + r, N - 1) - n0) * (int64_t)K) + (uint32_t)(p * 16);
+    }
+    const uint32_t woffs = (uint32_t)((min(n0 + 32 * wave + (lane >> 1), N - 1) - n0) * nb + 2 * (lane & 1)) * 2;
+    auto stage_copy = [&](int st, int b) {
         const int c0 = st * kKT;
+        if (c0 + kKT <= nb) {
 #pragma unroll
-        for (int it = 0; it < kKT * kTileBytes / 16 / 256; ++it) {
-            const int piece = it * 256 + wave * 64;  // first 16-byte piece of this wave
-            const int c = min(c0 + piece / (kTileBytes / 16), nb - 1);
-            const int8_t* src = plane + (int64_t)c * kTileBytes + (piece % (kTileBytes / 16)) * 16 + lane * 16;
-            lds_copy16(src, &lds_a[b][piece * 16]);
-        }
+            for (int it = 0; it < kKT * kTileBytes / 16 / 256; ++it)
+                lds_copy16(r_a, aoffs, (uint32_t)(c0 * kTileBytes + it * 4096), &lds_a[b][it * 4096 + wave * 1024]);
+            lds_copy4(r_s, soffs, (uint32_t)(c0 * kGroup * 4), &lds_s[b][wave * kGroup]);
 #pragma unroll
-        for (int it = 0; it < kKT * kGroup / 256; ++it) {
-            const int word = it * 256 + wave * 64;
-            const int c = min(c0 + word / kGroup, nb - 1);
-            lds_copy4(splane + (int64_t)c * kGroup + (word % kGroup) + lane, &lds_s[b][word]);
+            for (int it = 0; it < 4; ++it)
+                lds_copy16(r_b, boffs[it], (uint32_t)(c0 * kQK), &lds_b[b][(wave * 4 + it) * 1024]);
+            if constexpr (DWL) lds_copy4(r_w, woffs, (uint32_t)(c0 * 2), &lds_w[b][wave * 64]);
+        } else {
+#pragma unroll
+            for (int it = 0; it < kKT * kTileBytes / 16 / 256; ++it) {
+                const int c = min(c0 + 2 * it + wave / 2, nb - 1);  // chunk of this wave's piece
+                lds_copy16(r_a, (uint32_t)(c * kTileBytes + (wave & 1) * 1024 + lane * 16), 0u,
+                           &lds_a[b][it * 4096 + wave * 1024]);
+            }
+            lds_copy4(r_s, (uint32_t)((min(c0 + wave, nb - 1) * kGroup + lane) * 4), 0u, &lds_s[b][wave * kGroup]);
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int p = (lane & 7) ^ wsw(32 * wave + 8 * it + (lane >> 3));  // block p/2, half p%2
+                const int c = min(c0 + (p >> 1), nb - 1);
+                lds_copy16(r_b, boffs[it] + (uint32_t)((c - (p >> 1)) * kQK), 0u, &lds_b[b][(wave * 4 + it) * 1024]);
+            }
+            if constexpr (DWL) {
+                const int c = min(c0 + 2 * (lane & 1), nb - 2);
+                lds_copy4(r_w, woffs + (uint32_t)((c - 2 * (lane & 1)) * 2), 0u, &lds_w[b][wave * 64]);
+            }
         }
     };
-    auto stage_b = [&](int st, v4i (&bf)[kKT], uint32_t (&db)[kKT]) {
+    const _Float16* drow = reinterpret_cast<const _Float16*>(wd) + (nvalid ? nrow : 0) * (int64_t)nb;
+    auto load_dw = [&](int st, h2 (&db)[kKT / 2]) {  // the register form (!DWL)
 #pragma unroll
-        for (int kb = 0; kb < kKT; ++kb) {
-            const int c = min(st * kKT + kb, nb - 1);
-            bf[kb] = *reinterpret_cast<const v4i*>(wrow + (int64_t)c * kQK);
-            db[kb] = drow[c];
+        for (int i = 0; i < kKT / 2; ++i) {
+            h2 v;
+            v.x = drow[min(st * kKT + 2 * i, nb - 1)];
+            v.y = drow[min(st * kKT + 2 * i + 1, nb - 1)];
+            db[i] = v;
         }
     };
 
-    // Compute stage st from LDS buffer `buf` and weight fragments bf/db.
-    auto compute = [&](int st, int buf, const v4i (&bf)[kKT], const uint32_t (&db)[kKT]) {
-        const int kc = min(kKT, nb - st * kKT);
+    // Compute stage st from LDS buffer `buf` and weight scales db (two f16 per
+    // register: block 2i in the low half, 2i+1 in the high half). A tail stage
+    // runs the same straight-line code: its blocks past K hold copies of the
+    // last block and get a weight scale of 0, which adds an exact zero.
+    auto compute = [&](int st, int buf, h2 (&db)[kKT / 2]) {
+        const int kc = nb - st * kKT;  // blocks of this stage inside K (>= 1)
+        if (kc < kKT) {  // tail stage (wave-uniform): zero the scales of the blocks past K
+#pragma unroll
+            for (int kb = 1; kb < kKT; ++kb) {
+                if (kb >= kc) {
+                    if (kb & 1)
+                        db[kb / 2].y = (_Float16)0.0f;
+                    else
+                        db[kb / 2].x = (_Float16)0.0f;
+                }
+            }
+        }
         const int8_t* la = &lds_a[buf][0];
+        const int8_t* lb = &lds_b[buf][0];
         const uint32_t* ls = &lds_s[buf][0];
-        auto frags = [&](int kb, v4i (&af)[2], uint32_t (&sc)[2]) {
+        auto frags = [&](int kb, v4i (&af)[2], v4i& bf, uint32_t (&sc)[2]) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 af[h] = *reinterpret_cast<const v4i*>(la + kb * kTileBytes + aoff[h]);
                 sc[h] = ls[kb * kGroup + 32 * h + srow];
             }
+            bf = *reinterpret_cast<const v4i*>(lb + (boff ^ (32 * kb)));
         };
-        // Pipeline over the 2*nk (block, half) tiles: the MFMA of the next tile is
-        // issued before the epilogue of the current one, and the A fragments of
+        // Pipeline over the 2*kKT (block, half) tiles: the MFMA of the next tile
+        // is issued before the epilogue of the current one, and the fragments of
         // block kb+1 are read from LDS while block kb is being finished.
-        auto run = [&](auto nk) {  // nk: std::integral_constant for full stages, int for the tail
-            v4i af[2], an[2];
-            uint32_t sc[2], sn[2];
-            frags(0, af, sc);
-            v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[0], bf[0], bias, 0, 0, 0);
+        v4i af[2], an[2], bf, bn;
+        uint32_t sc[2], sn[2];
+        frags(0, af, bf, sc);
+        v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[0], bf, bias, 0, 0, 0);
 #pragma unroll
-            for (int kb = 0; kb < kKT; ++kb) {
-                if (kb < nk) {
-                    const float dw = nvalid ? f16_value(db[kb]) : 0.0f;
-                    const float nbias = -kBiasF * dw;
-                    if (kb + 1 < nk) frags(kb + 1, an, sn);
-                    // tile (kb, 0) is in d; start (kb, 1)
-                    const v16i d0 = d;
-                    d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[1], bf[kb], bias, 0, 0, 0);
-                    epilogue(acc[0], __builtin_bit_cast(v16f, d0), dw, nbias, f16_value(sc[0]));
-                    // tile (kb, 1) is in d; start (kb + 1, 0)
-                    const v16i d1 = d;
-                    if (kb + 1 < nk) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(an[0], bf[kb + 1], bias, 0, 0, 0);
-                    epilogue(acc[1], __builtin_bit_cast(v16f, d1), dw, nbias, f16_value(sc[1]));
-                    af[0] = an[0];
-                    af[1] = an[1];
-                    sc[0] = sn[0];
-                    sc[1] = sn[1];
-                }
-            }
-        };
-        if (kc == kKT)
-            run(std::integral_constant<int, kKT>{});  // full stage: straight-line code, no joins
-        else
-            run(kc);
+        for (int kb = 0; kb < kKT; ++kb) {
+            // (lanes of rows past N compute with row N-1's data and store nothing)
+            const float dw = (float)((kb & 1) ? db[kb / 2].y : db[kb / 2].x);
+            const float nbias = -kBiasF * dw;
+            if (kb + 1 < kKT) frags(kb + 1, an, bn, sn);
+            // tile (kb, 0) is in d; start (kb, 1)
+            const v16i d0 = d;
+            d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[1], bf, bias, 0, 0, 0);
+            epilogue(acc[0], __builtin_bit_cast(v16f, d0), dw, nbias, f16_value(sc[0]));
+            // tile (kb, 1) is in d; start (kb + 1, 0)
+            const v16i d1 = d;
+            if (kb + 1 < kKT) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(an[0], bn, bias, 0, 0, 0);
+            epilogue(acc[1], __builtin_bit_cast(v16f, d1), dw, nbias, f16_value(sc[1]));
+            af[0] = an[0];
+            af[1] = an[1];
+            bf = bn;
+            sc[0] = sn[0];
+            sc[1] = sn[1];
+        }
+    };
+    auto lds_dw = [&](int buf, h2 (&db)[kKT / 2]) {
+        const uint2 v = *reinterpret_cast<const uint2*>(&lds_w[buf][brow * 2]);
+        db[0] = __builtin_bit_cast(h2, v.x);
+        db[1] = __builtin_bit_cast(h2, v.y);
     };
 
-    // Two register sets for the weight fragments, used alternately, so stage
-    // st+1's fragments load while stage st computes without any copies.
-    v4i b0[kKT], b1[kKT];
-    uint32_t d0[kKT], d1[kKT];
-    stage_a(0, 0);
-    stage_b(0, b0, d0);
-    __syncthreads();  // the compiler drains the copies (vmcnt) before the barrier
+    // Each wave waits for its own copies (vmcnt) before the barrier that
+    // publishes the stage to the other waves.
+    h2 d0[kKT / 2], d1[kKT / 2];
+    stage_copy(0, 0);
+    if constexpr (!DWL) load_dw(0, d0);
+    wait_copies();
+    __syncthreads();
     for (int st = 0; st < nst; st += 2) {
         if (st + 1 < nst) {
-            stage_a(st + 1, 1);
-            stage_b(st + 1, b1, d1);
+            stage_copy(st + 1, 1);
+            if constexpr (!DWL) load_dw(st + 1, d1);
         }
-        compute(st, 0, b0, d0);
+        if constexpr (DWL) lds_dw(0, d0);
+        compute(st, 0, d0);
+        wait_copies();
         __syncthreads();
         if (st + 1 < nst) {
             if (st + 2 < nst) {
-                stage_a(st + 2, 0);
-                stage_b(st + 2, b0, d0);
+                stage_copy(st + 2, 0);
+                if constexpr (!DWL) load_dw(st + 2, d0);
             }
-            compute(st + 1, 1, b1, d1);
+            if constexpr (DWL) lds_dw(1, d1);
+            compute(st + 1, 1, d1);
+            wait_copies();
             __syncthreads();
         }
     }
@@ -247,7 +360,8 @@ __global__ __launch_bounds__(256) void k_gemm(const int8_t* __restrict__ aq, con
 extern "C" int q8_gemm(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t, float* c,
                        int64_t ldc, void* stream) {
     if (W == nullptr) return Q8_EINVAL;
-    if (W->n < 0 || W->k <= 0 || (W->k % kQK) != 0 || W->k > ((int64_t)1 << 30) || t < 0) return Q8_ESHAPE;
+    // K <= 2^24 keeps every in-tile byte offset of the weight copies in 32 bits.
+    if (W->n < 0 || W->k <= 0 || (W->k % kQK) != 0 || W->k > ((int64_t)1 << 24) || t < 0) return Q8_ESHAPE;
     if (ldc < W->n) return Q8_ESHAPE;
     if (t == 0 || W->n == 0) return Q8_OK;
     if (W->qs == nullptr || W->d == nullptr || a_qs == nullptr || a_sd == nullptr || c == nullptr) return Q8_EINVAL;
@@ -259,7 +373,11 @@ extern "C" int q8_gemm(const q8_weights* W, const int8_t* a_qs, const uint32_t* 
     const int64_t n_tiles = q8h::ceil_div(W->n, kBN);
     const int64_t tiles = n_tiles * ntb;
     if (tiles > INT32_MAX) return Q8_ESHAPE;
-    hipLaunchKernelGGL(k_gemm, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, a_qs, a_sd, W->qs, W->d, c,
-                       t, W->n, (int)W->k, nb, ldc, (int)n_tiles, tiles);
+    if (nb % 2 == 0 && q8h::aligned(W->d, 4))  // 4-byte scale pairs
+        hipLaunchKernelGGL(k_gemm<true>, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, a_qs, a_sd, W->qs,
+                           W->d, c, t, W->n, (int)W->k, nb, ldc, (int)n_tiles, tiles);
+    else
+        hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, a_qs, a_sd,
+                           W->qs, W->d, c, t, W->n, (int)W->k, nb, ldc, (int)n_tiles, tiles);
     return q8h::launch_status();
 }

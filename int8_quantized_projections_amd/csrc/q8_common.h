@@ -118,11 +118,12 @@ __device__ __forceinline__ Quant8 quantize_block8(float4 v) {
 
 // Workgroups are dealt to the 8 XCDs in turn (workgroup p runs on XCD p % 8).
 // Remap a linear workgroup index so that each XCD gets one contiguous range
-// of logical indices: neighbouring rows then share an XCD, so the 64 rows of
-// a plane tile are assembled in one L2 instead of eight.
+// of logical indices (the first count % 8 XCDs one more than the others):
+// neighbouring work items then share an XCD and its L2, e.g. the 64 rows of a
+// plane tile, or the GEMM tiles that read the same operand strips.
 __device__ __forceinline__ int64_t xcd_contiguous(int64_t p, int64_t count) {
-    if (count % 8 != 0) return p;
-    return (p % 8) * (count / 8) + p / 8;
+    const int64_t x = p % 8, q = count / 8, r = count % 8;
+    return x * q + (x < r ? x : r) + p / 8;
 }
 
 // PLANE64 addressing. Byte offset, inside the qs plane, of the 4-byte group

@@ -110,6 +110,7 @@ def test_gemv_and_gemm_reject_before_launch(L):
     assert L.q8_gemm(ctypes.byref(w), None, f, 5, f, 8, None) == Q8_EINVAL
     assert L.q8_gemm(ctypes.byref(w), f, f + 1, 5, f, 8, None) == Q8_EALIGN
     assert L.q8_gemm(ctypes.byref(w), f, f, 0, f, 8, None) == Q8_OK  # T = 0: no-op
+    assert L.q8_gemm(ctypes.byref(_w(8, (1 << 24) + 32)), f, f, 5, f, 8, None) == Q8_ESHAPE  # K > 2^24
     assert L.q8_weights_repack(f + 1, 4, 64, f, f, None) == Q8_EALIGN
     assert L.q8_weights_repack(f, 4, 65, f, f, None) == Q8_ESHAPE
 

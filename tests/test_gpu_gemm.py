@@ -103,3 +103,24 @@ def test_gemm_deterministic():
     b = run_gemm(W, pq, ps, T)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("K", [3584, 2080])
+def test_gemm_scale_plane_two_byte_aligned(K):
+    """A weight-scale plane that is only 2-byte aligned (allowed by the interface)
+    takes the per-lane scale loads instead of the 4-byte pair copies; the two
+    forms give identical bits."""
+    T, N = 130, 200
+    x = synth.normal((T, K), stream=5500)
+    W, wq, wd = weights(synth.normal((N, K), stream=5501, std=0.02))
+    pq, ps, qo, do, _ = plane_act(x)
+    buf = torch.empty(W.d.numel() + 1, dtype=torch.int16, device=W.d.device)
+    buf[1:] = W.d.reshape(-1)
+    W2 = q8lib.Q8Weights(W.qs, buf[1:].view(W.d.shape))  # data pointer = 2 mod 4
+    assert W2.d.data_ptr() % 4 == 2
+    C1 = run_gemm(W, pq, ps, T)
+    C2 = run_gemm(W2, pq, ps, T)
+    torch.cuda.synchronize()
+    ref, norm = oracle.gemm(wq, wd, qo, do)
+    assert_norm(to_np(C2), ref, norm, 1e-5, f"gemm 2-byte-aligned scales K={K}")
+    assert torch.equal(C1, C2)
