@@ -38,6 +38,9 @@ namespace {
 
 constexpr int kBN = 128;  // weight rows per workgroup
 constexpr int kKT = 4;    // K blocks per LDS stage (double-buffered)
+constexpr int kPR = 2 * kKT;          // 16-byte pieces of a weight row per stage
+constexpr int kRowB = kKT * 32;       // bytes of a weight row per stage
+static_assert(kKT == 2 || kKT == 4, "stage of 2 or 4 blocks");
 constexpr int kBias = 0x4B400000;
 constexpr float kBiasF = 12582912.0f;  // 1.5 * 2^23
 
@@ -125,12 +128,15 @@ __device__ __forceinline__ void tile_of(int64_t p, int64_t tiles, int n_tiles, i
     }
 }
 
-// Weight tile in LDS: 128 rows of 128 bytes (4 blocks); the 16-byte piece p
-// (block p/2, half p%2) of tile row r sits at slot 8r + (p ^ wsw(r)). The copy
-// reads each row's 128 bytes with 8 consecutive lanes (whole cache lines), and
-// the fragment read (32 consecutive rows, one piece) touches every bank group
-// once per 8 or 16 lanes.
-__device__ __forceinline__ int wsw(int r) { return (r ^ (r >> 3)) & 7; }
+// Weight tile in LDS: 128 rows of kRowB bytes (kKT blocks); the 16-byte piece
+// p (block p/2, half p%2) of tile row r sits at slot kPR*r + (p ^ wsw(r)). The
+// copy reads each row's bytes with kPR consecutive lanes (whole cache-line
+// runs), and the fragment read (32 consecutive rows, one piece) touches every
+// bank group once per 8 or 16 lanes.
+__device__ __forceinline__ int wsw(int r) {
+    if constexpr (kPR == 8) return (r ^ (r >> 3)) & 7;
+    return ((r >> 1) ^ (r >> 3)) & 3;
+}
 
 // DWL: the weight scales of a stage are copied into LDS with 4-byte copies of
 // block pairs, which needs K/32 even (4-byte aligned pairs); otherwise every
@@ -147,6 +153,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     __shared__ __attribute__((aligned(16))) int8_t lds_b[2][kBN * kKT * kQK];
     __shared__ __attribute__((aligned(16))) uint32_t lds_s[2][kKT * kGroup];
     __shared__ __attribute__((aligned(16))) uint32_t lds_w[2][DWL ? kBN * kKT / 2 : 1];
+    static_assert(kKT * kGroup <= 256 && kBN * kKT / 2 <= 256, "one scale copy per wave at most");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -172,7 +179,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const int i = 32 * h + (lane & 31);
         aoff[h] = i * 32 + (((khalf ^ (i >> 2) ^ (i >> 3)) & 1) * 16);
     }
-    const int boff = brow * 128 + 16 * (khalf ^ wsw(brow));
+    const int boff = brow * kRowB + 16 * (khalf ^ wsw(brow));
 
     v16i bias;
 #pragma unroll
@@ -203,25 +210,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const __amdgpu_buffer_rsrc_t r_w = make_rsrc(wd + n0 * (int64_t)nb, (N - n0) * (int64_t)nb * 2);
     const uint32_t aoffs = (uint32_t)(wave * 1024 + lane * 16);  // + 4096 * it
     const uint32_t soffs = (uint32_t)(wave * kGroup + lane) * 4;
-    uint32_t boffs[4];  // this lane's copy `it`: byte offset from the tile's first row, block 0
+    // weights: wave w copies tile rows 32w .. 32w+31, 64/kPR rows per instruction
+    auto brow_of = [&](int it) { return 32 * wave + (64 / kPR) * it + lane / kPR; };
+    auto piece_of = [&](int it) { return (lane % kPR) ^ wsw(brow_of(it)); };  // block p/2, half p%2
+    uint32_t boffs[kKT];  // this lane's copy `it`: byte offset from the tile's first row, block 0
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int r = 32 * wave + 8 * it + (lane >> 3);
-        const int p = (lane & 7) ^ wsw(r);
-        boffs[it] = (uint32_t)((min(n0 + r, N - 1) - n0) * (int64_t)K) + (uint32_t)(p * 16);
-    }
-    const uint32_t woffs = (uint32_t)((min(n0 + 32 * wave + (lane >> 1), N - 1) - n0) * nb + 2 * (lane & 1)) * 2;
+    for (int it = 0; it < kKT; ++it)
+        boffs[it] = (uint32_t)((min(n0 + brow_of(it), N - 1) - n0) * (int64_t)K) + (uint32_t)(piece_of(it) * 16);
+    // weight scales: copy instruction w (w < kKT) takes rows (128/kKT)w .., kKT/2 block pairs per row
+    constexpr int kPairs = kKT / 2;
+    const int wpair = lane % kPairs;
+    const uint32_t woffs =
+        (uint32_t)((min(n0 + (128 / kKT) * wave + lane / kPairs, N - 1) - n0) * nb + 2 * wpair) * 2;
     auto stage_copy = [&](int st, int b) {
         const int c0 = st * kKT;
         if (c0 + kKT <= nb) {
 #pragma unroll
             for (int it = 0; it < kKT * kTileBytes / 16 / 256; ++it)
                 lds_copy16(r_a, aoffs, (uint32_t)(c0 * kTileBytes + it * 4096), &lds_a[b][it * 4096 + wave * 1024]);
-            lds_copy4(r_s, soffs, (uint32_t)(c0 * kGroup * 4), &lds_s[b][wave * kGroup]);
+            if (wave < kKT) lds_copy4(r_s, soffs, (uint32_t)(c0 * kGroup * 4), &lds_s[b][wave * kGroup]);
 #pragma unroll
-            for (int it = 0; it < 4; ++it)
-                lds_copy16(r_b, boffs[it], (uint32_t)(c0 * kQK), &lds_b[b][(wave * 4 + it) * 1024]);
-            if constexpr (DWL) lds_copy4(r_w, woffs, (uint32_t)(c0 * 2), &lds_w[b][wave * 64]);
+            for (int it = 0; it < kKT; ++it)
+                lds_copy16(r_b, boffs[it], (uint32_t)(c0 * kQK), &lds_b[b][(wave * kKT + it) * 1024]);
+            if constexpr (DWL)
+                if (wave < kKT) lds_copy4(r_w, woffs, (uint32_t)(c0 * 2), &lds_w[b][wave * 64]);
         } else {
 #pragma unroll
             for (int it = 0; it < kKT * kTileBytes / 16 / 256; ++it) {
@@ -229,16 +241,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 lds_copy16(r_a, (uint32_t)(c * kTileBytes + (wave & 1) * 1024 + lane * 16), 0u,
                            &lds_a[b][it * 4096 + wave * 1024]);
             }
-            lds_copy4(r_s, (uint32_t)((min(c0 + wave, nb - 1) * kGroup + lane) * 4), 0u, &lds_s[b][wave * kGroup]);
+            if (wave < kKT)
+                lds_copy4(r_s, (uint32_t)((min(c0 + wave, nb - 1) * kGroup + lane) * 4), 0u, &lds_s[b][wave * kGroup]);
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int p = (lane & 7) ^ wsw(32 * wave + 8 * it + (lane >> 3));  // block p/2, half p%2
+            for (int it = 0; it < kKT; ++it) {
+                const int p = piece_of(it);
                 const int c = min(c0 + (p >> 1), nb - 1);
-                lds_copy16(r_b, boffs[it] + (uint32_t)((c - (p >> 1)) * kQK), 0u, &lds_b[b][(wave * 4 + it) * 1024]);
+                lds_copy16(r_b, boffs[it] + (uint32_t)((c - (p >> 1)) * kQK), 0u,
+                           &lds_b[b][(wave * kKT + it) * 1024]);
             }
             if constexpr (DWL) {
-                const int c = min(c0 + 2 * (lane & 1), nb - 2);
-                lds_copy4(r_w, woffs + (uint32_t)((c - 2 * (lane & 1)) * 2), 0u, &lds_w[b][wave * 64]);
+                if (wave < kKT) {
+                    const int c = min(c0 + 2 * wpair, nb - 2);
+                    lds_copy4(r_w, woffs + (uint32_t)((c - 2 * wpair) * 2), 0u, &lds_w[b][wave * 64]);
+                }
             }
         }
     };
@@ -291,7 +307,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
         for (int kb = 0; kb < kKT; ++kb) {
             // (lanes of rows past N compute with row N-1's data and store nothing)
-            const float dw = (float)((kb & 1) ? db[kb / 2].y : db[kb / 2].x);
+            float dw = (float)((kb & 1) ? db[kb / 2].y : db[kb / 2].x);
+            // Opaque after the conversion, so the 32 FMAs below stay plain v_fma_f32:
+            // folding the f16 operand into v_fma_mix_f32 makes each of them about
+            // 1.5x as expensive on gfx950.
+            asm volatile("" : "+v"(dw));
             const float nbias = -kBiasF * dw;
             if (kb + 1 < kKT) frags(kb + 1, an, bn, sn);
             // tile (kb, 0) is in d; start (kb, 1)
@@ -310,9 +330,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         }
     };
     auto lds_dw = [&](int buf, h2 (&db)[kKT / 2]) {
-        const uint2 v = *reinterpret_cast<const uint2*>(&lds_w[buf][brow * 2]);
-        db[0] = __builtin_bit_cast(h2, v.x);
-        db[1] = __builtin_bit_cast(h2, v.y);
+        if constexpr (kKT == 4) {
+            const uint2 v = *reinterpret_cast<const uint2*>(&lds_w[buf][brow * 2]);
+            db[0] = __builtin_bit_cast(h2, v.x);
+            db[1] = __builtin_bit_cast(h2, v.y);
+        } else {
+            db[0] = __builtin_bit_cast(h2, lds_w[buf][brow]);
+        }
     };
 
     // Each wave waits for its own copies (vmcnt) before the barrier that
