@@ -333,12 +333,21 @@ def bench_prefill_rms(D, reps):
     b = rms_bytes(T, K, 1)
     out["rmsnorm_quant_plane64"] = {**t, "bytes": b, "GBps": b / t["mean_us"] / 1e3,
                                     "frac_hbm": b / t["mean_us"] / 1e3 / HBM_PEAK_GBS}
-    total_us = t["mean_us"]
+    prod_us = t["mean_us"]
+    sep_us = 0.0
     for n, W in Ws.items():
         t = stats(time_each(D, lambda i, W=W, n=n: q8.q8_gemm(W, pq, ps, T, C[n]), reps))
         out[f"q8_gemm_{W.n}x{K}"] = gemm_entry(t, T, W.n, K)
-        total_us += t["mean_us"]
-    out["slice_tok_per_s"] = T / (total_us * 1e-6)
+        sep_us += t["mean_us"]
+    # q, k and v over the one plane in one grouped launch (what the slice uses)
+    names = list(Ws)
+    t = stats(time_each(D, lambda i: q8.q8_gemm_shared_multi([Ws[n] for n in names], pq, ps, T,
+                                                              [C[n] for n in names]), reps))
+    n_all = sum(W.n for W in Ws.values())
+    out[f"q8_gemm_shared_multi_qkv_{n_all}x{K}"] = gemm_entry(t, T, n_all, K)
+    out["slice_launches"] = 2
+    out["slice_tok_per_s"] = T / ((prod_us + t["mean_us"]) * 1e-6)
+    out["slice_tok_per_s_separate_gemms"] = T / ((prod_us + sep_us) * 1e-6)
     return out
 
 

@@ -167,6 +167,20 @@ int q8_gemm(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64
             void* stream);
 
 /*
+ * Several prefill GEMMs that read the same PLANE64 activation, in one launch:
+ * the prefill counterpart of q8_gemv_shared_multi ([P1] s2.5, s6: consumers of
+ * one activation in one grouped kernel; [P2] s1: q/k/v read one plane).
+ * m: 1..8. W: host array of m host pointers, all with the same k. c: host
+ * array of m device pointers; ldc: host array of m values; c[i] is
+ * [T][ldc[i]] f32 with ldc[i] >= W[i]->n. Members with n == 0 are skipped.
+ * Each c[i] is bit-identical to q8_gemm(W[i], a_qs, a_sd, t, c[i], ldc[i]).
+ * Returns Q8_EINVAL (m out of range, NULL), Q8_ESHAPE (k differs, ldc < n,
+ * K > 2^24, t < 0) or Q8_EALIGN before any launch.
+ */
+int q8_gemm_shared_multi(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t,
+                         float* const* c, const int64_t* ldc, void* stream);
+
+/*
  * Load-time conversion of GGUF Q8_0 blocks (device, [N][K/32] x 34 bytes,
  * 2-byte aligned; [P1] s2.1) into the weight planes qs [N][K] and d [N][K/32]
  * (device). Pure byte movement.

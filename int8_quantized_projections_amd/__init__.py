@@ -14,6 +14,7 @@ from .q8lib import (  # noqa: F401
     alloc_act,
     gemv_plan,
     q8_gemm,
+    q8_gemm_shared_multi,
     q8_gemv,
     q8_gemv_shared_multi,
     q8_quantize,

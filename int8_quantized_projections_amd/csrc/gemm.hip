@@ -104,6 +104,30 @@ __device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t r, uint32_t vof
 // (s_waitcnt vmcnt(0); the expcnt and lgkmcnt fields are left at their maxima).
 __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// The weight matrices of one launch: q8_gemm passes one, q8_gemm_shared_multi
+// up to kMaxMembers that read the same activation plane. Their n-tiles are
+// concatenated; member i owns tiles [tile0[i], tile0[i+1]).
+constexpr int kMaxMembers = 8;
+struct GemmMembers {
+    const int8_t* wq[kMaxMembers];
+    const uint16_t* wd[kMaxMembers];
+    float* c[kMaxMembers];
+    int64_t n[kMaxMembers];
+    int64_t ldc[kMaxMembers];
+    int tile0[kMaxMembers + 1];
+    int m;
+};
+
+// a[i] for a wave-uniform i, as a chain of selects (a dynamic index into the
+// by-value kernel argument would make the compiler copy it to scratch).
+template <typename T>
+__device__ __forceinline__ T pick(const T (&a)[kMaxMembers], int i) {
+    T v = a[0];
+#pragma unroll
+    for (int j = 1; j < kMaxMembers; ++j) v = (i == j) ? a[j] : v;
+    return v;
+}
+
 // Tile order: the n-tiles are cut into panels of kPanel; a panel's tiles are
 // taken token group by token group. With each XCD given a contiguous range of
 // this order, the ~96 tiles resident on one XCD span about 8 n-tiles x 12
@@ -143,8 +167,7 @@ __device__ __forceinline__ int wsw(int r) {
 // lane loads its own row's scales into registers one stage ahead.
 template <bool DWL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm(
-    const int8_t* __restrict__ aq, const uint32_t* __restrict__ asd, const int8_t* __restrict__ wq,
-    const uint16_t* __restrict__ wd, float* __restrict__ C, int64_t T, int64_t N, int K, int nb, int64_t ldc,
+    const int8_t* __restrict__ aq, const uint32_t* __restrict__ asd, const GemmMembers M, int64_t T, int K, int nb,
     int n_tiles, int64_t tiles) {
     // Double-buffered stage: kKT chunks of one 64-token group of the A plane
     // (verbatim) with their scale words, and kKT blocks of the 128 weight rows
@@ -160,6 +183,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     int nt;
     int64_t g;
     tile_of(blockIdx.x, tiles, n_tiles, nt, g);
+    // the member this tile belongs to (wave-uniform) and the tile inside it
+    int mi = 0, tbase = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxMembers; ++i) {
+        if (i < M.m && nt >= M.tile0[i]) {
+            mi = i;
+            tbase = M.tile0[i];
+        }
+    }
+    nt -= tbase;
+    const int8_t* __restrict__ wq = pick(M.wq, mi);
+    const uint16_t* __restrict__ wd = pick(M.wd, mi);
+    float* __restrict__ C = pick(M.c, mi);
+    const int64_t N = pick(M.n, mi);
+    const int64_t ldc = pick(M.ldc, mi);
     const int64_t n0 = (int64_t)nt * kBN;
     const int brow = wave * 32 + (lane & 31);  // this lane's weight row in the tile
     const int64_t nrow = n0 + brow;            // and its output column
@@ -381,27 +419,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
 }  // namespace
 
-extern "C" int q8_gemm(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t, float* c,
-                       int64_t ldc, void* stream) {
+namespace {
+
+// Validation shared by q8_gemm and q8_gemm_shared_multi (the activation side is
+// checked by the caller).
+int check_member(const q8_weights* W, int64_t ldc, const float* c) {
     if (W == nullptr) return Q8_EINVAL;
     // K <= 2^24 keeps every in-tile byte offset of the weight copies in 32 bits.
-    if (W->n < 0 || W->k <= 0 || (W->k % kQK) != 0 || W->k > ((int64_t)1 << 24) || t < 0) return Q8_ESHAPE;
+    if (W->n < 0 || W->k <= 0 || (W->k % kQK) != 0 || W->k > ((int64_t)1 << 24)) return Q8_ESHAPE;
     if (ldc < W->n) return Q8_ESHAPE;
-    if (t == 0 || W->n == 0) return Q8_OK;
-    if (W->qs == nullptr || W->d == nullptr || a_qs == nullptr || a_sd == nullptr || c == nullptr) return Q8_EINVAL;
-    if (!q8h::aligned(W->qs, 16) || !q8h::aligned(W->d, 2) || !q8h::aligned(a_qs, 16) || !q8h::aligned(a_sd, 4) ||
-        !q8h::aligned(c, 4))
-        return Q8_EALIGN;
-    const int nb = (int)(W->k / kQK);
-    const int64_t ntb = q8h::ceil_div(t, kGroup);
-    const int64_t n_tiles = q8h::ceil_div(W->n, kBN);
-    const int64_t tiles = n_tiles * ntb;
+    if (W->n == 0) return Q8_OK;
+    if (W->qs == nullptr || W->d == nullptr || c == nullptr) return Q8_EINVAL;
+    if (!q8h::aligned(W->qs, 16) || !q8h::aligned(W->d, 2) || !q8h::aligned(c, 4)) return Q8_EALIGN;
+    return Q8_OK;
+}
+
+int launch_gemm(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t,
+                float* const* c, const int64_t* ldc, hipStream_t stream) {
+    if (m < 1 || m > kMaxMembers || W == nullptr || c == nullptr || ldc == nullptr) return Q8_EINVAL;
+    if (t < 0) return Q8_ESHAPE;
+    int rc;
+    for (int i = 0; i < m; ++i) {
+        if ((rc = check_member(W[i], ldc[i], c[i]))) return rc;
+        if (W[i]->k != W[0]->k) return Q8_ESHAPE;
+    }
+    if (a_qs == nullptr || a_sd == nullptr) return Q8_EINVAL;
+    if (!q8h::aligned(a_qs, 16) || !q8h::aligned(a_sd, 4)) return Q8_EALIGN;
+    if (t == 0) return Q8_OK;
+    GemmMembers M = {};
+    const int nb = (int)(W[0]->k / kQK);
+    bool pairs = nb % 2 == 0;  // 4-byte scale pairs in LDS for every member, else the register form
+    int64_t n_tiles = 0;
+    M.m = 0;
+    for (int i = 0; i < m; ++i) {
+        if (W[i]->n == 0) continue;  // nothing to compute or write
+        const int j = M.m++;
+        M.wq[j] = W[i]->qs;
+        M.wd[j] = W[i]->d;
+        M.c[j] = c[i];
+        M.n[j] = W[i]->n;
+        M.ldc[j] = ldc[i];
+        M.tile0[j] = (int)n_tiles;
+        n_tiles += q8h::ceil_div(W[i]->n, kBN);
+        pairs = pairs && q8h::aligned(W[i]->d, 4);
+        if (n_tiles > INT32_MAX) return Q8_ESHAPE;
+    }
+    if (M.m == 0) return Q8_OK;
+    M.tile0[M.m] = (int)n_tiles;
+    for (int j = M.m; j < kMaxMembers; ++j) {  // unused slots repeat the last member (never selected)
+        M.wq[j] = M.wq[M.m - 1];
+        M.wd[j] = M.wd[M.m - 1];
+        M.c[j] = M.c[M.m - 1];
+        M.n[j] = M.n[M.m - 1];
+        M.ldc[j] = M.ldc[M.m - 1];
+        M.tile0[j + 1] = (int)n_tiles;
+    }
+    const int64_t tiles = n_tiles * q8h::ceil_div(t, kGroup);
     if (tiles > INT32_MAX) return Q8_ESHAPE;
-    if (nb % 2 == 0 && q8h::aligned(W->d, 4))  // 4-byte scale pairs
-        hipLaunchKernelGGL(k_gemm<true>, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, a_qs, a_sd, W->qs,
-                           W->d, c, t, W->n, (int)W->k, nb, ldc, (int)n_tiles, tiles);
+    if (pairs)
+        hipLaunchKernelGGL(k_gemm<true>, dim3((unsigned)tiles), dim3(256), 0, stream, a_qs, a_sd, M, t,
+                           (int)W[0]->k, nb, (int)n_tiles, tiles);
     else
-        hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, a_qs, a_sd,
-                           W->qs, W->d, c, t, W->n, (int)W->k, nb, ldc, (int)n_tiles, tiles);
+        hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)tiles), dim3(256), 0, stream, a_qs, a_sd, M, t,
+                           (int)W[0]->k, nb, (int)n_tiles, tiles);
     return q8h::launch_status();
+}
+
+}  // namespace
+
+extern "C" int q8_gemm(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t, float* c,
+                       int64_t ldc, void* stream) {
+    return launch_gemm(1, &W, a_qs, a_sd, t, &c, &ldc, (hipStream_t)stream);
+}
+
+extern "C" int q8_gemm_shared_multi(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
+                                    int64_t t, float* const* c, const int64_t* ldc, void* stream) {
+    return launch_gemm(m, W, a_qs, a_sd, t, c, ldc, (hipStream_t)stream);
 }

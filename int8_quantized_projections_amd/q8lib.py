@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
             "q8_gemv_shared_multi_ex": ([ci, ctypes.POINTER(wp), vp, vp, ctypes.POINTER(vp), ci, vp], ci),
             "q8_gemv_plan": ([i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(i64)], ci),
             "q8_gemm": ([wp, vp, vp, i64, vp, i64, vp], ci),
+            "q8_gemm_shared_multi": ([ci, ctypes.POINTER(wp), vp, vp, i64, ctypes.POINTER(vp), ctypes.POINTER(i64), vp],
+                                     ci),
             "q8_weights_repack": ([vp, i64, i64, vp, vp, vp], ci),
         }
         for name, (args, res) in sig.items():
@@ -228,3 +230,20 @@ def q8_gemm(W: Q8Weights, a_qs: torch.Tensor, a_sd: torch.Tensor, t: int, C=None
     ws = W.struct()
     _check(lib().q8_gemm(ctypes.byref(ws), _ptr(a_qs), _ptr(a_sd), t, _ptr(C), ldc, _stream(a_qs.device)), "q8_gemm")
     return C
+
+
+def q8_gemm_shared_multi(Ws: list[Q8Weights], a_qs: torch.Tensor, a_sd: torch.Tensor, t: int, Cs=None,
+                         ldcs: list[int] | None = None) -> list[torch.Tensor]:
+    """One launch of q8_gemm for every W in Ws over the same PLANE64 activation."""
+    m = len(Ws)
+    if Cs is None:
+        Cs = [torch.empty((t, W.n), dtype=torch.float32, device=a_qs.device) for W in Ws]
+    if ldcs is None:
+        ldcs = [C.shape[-1] if C.dim() > 1 else W.n for C, W in zip(Cs, Ws)]
+    structs = [W.struct() for W in Ws]
+    wps = (ctypes.POINTER(_Weights) * m)(*[ctypes.pointer(s) for s in structs])
+    cps = (ctypes.c_void_p * m)(*[_ptr(C) for C in Cs])
+    lds = (ctypes.c_int64 * m)(*ldcs)
+    _check(lib().q8_gemm_shared_multi(m, wps, _ptr(a_qs), _ptr(a_sd), t, cps, lds, _stream(a_qs.device)),
+           "q8_gemm_shared_multi")
+    return Cs

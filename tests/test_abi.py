@@ -111,6 +111,22 @@ def test_gemv_and_gemm_reject_before_launch(L):
     assert L.q8_gemm(ctypes.byref(w), f, f + 1, 5, f, 8, None) == Q8_EALIGN
     assert L.q8_gemm(ctypes.byref(w), f, f, 0, f, 8, None) == Q8_OK  # T = 0: no-op
     assert L.q8_gemm(ctypes.byref(_w(8, (1 << 24) + 32)), f, f, 5, f, 8, None) == Q8_ESHAPE  # K > 2^24
+    # grouped gemm: m range, K must agree, every member's ldc and pointers checked
+    def grouped(ws, cs, ldcs, t=5, aq=f, asd=f, m=None):
+        wa = (ctypes.POINTER(q8lib._Weights) * len(ws))(*[ctypes.pointer(x) for x in ws])
+        ca = (ctypes.c_void_p * len(cs))(*cs)
+        la = (ctypes.c_int64 * len(ldcs))(*ldcs)
+        return L.q8_gemm_shared_multi(len(ws) if m is None else m, wa, aq, asd, t, ca, la, None)
+    assert grouped([_w(8, 64), _w(8, 64)], [f, f], [8, 8], m=0) == Q8_EINVAL
+    assert grouped([_w(8, 64)] * 9, [f] * 9, [8] * 9) == Q8_EINVAL
+    assert grouped([_w(8, 64), _w(8, 96)], [f, f], [8, 8]) == Q8_ESHAPE  # K differs
+    assert grouped([_w(8, 64), _w(16, 64)], [f, f], [8, 8]) == Q8_ESHAPE  # ldc < N of member 1
+    assert grouped([_w(8, 64), _w(8, 64)], [f, None], [8, 8]) == Q8_EINVAL
+    assert grouped([_w(8, 64), _w(8, 64)], [f, f + 2], [8, 8]) == Q8_EALIGN
+    assert grouped([_w(8, 64)], [f], [8], aq=None) == Q8_EINVAL
+    assert grouped([_w(8, 64)], [f], [8], t=-1) == Q8_ESHAPE
+    assert grouped([_w(8, 64), _w(8, 64)], [f, f], [8, 8], t=0) == Q8_OK  # T = 0: no-op
+    assert grouped([_w(0, 64), _w(0, 64)], [f, f], [0, 0]) == Q8_OK  # every member empty: no-op
     assert L.q8_weights_repack(f + 1, 4, 64, f, f, None) == Q8_EALIGN
     assert L.q8_weights_repack(f, 4, 65, f, f, None) == Q8_ESHAPE
 

@@ -115,9 +115,20 @@ def test_prefill_rms_full():
     assert torch.equal(pq_f, pq2) and torch.equal(ps_f, ps2), "fused plane differs from standalone"
     del y, pq2, ps2
     pq, ps, qo, do, _ = plane_act(y_ref.astype(np.float32))
-    for n in ("Wq", "Wk", "Wv"):
-        W, wq, wd = workload_weights(wl, n)
-        check_gemm_cells(W, wq, wd, qo, do, pq, ps, T, f"gemm {n} T={T}")
+    # q, k and v in one grouped launch, as the benchmark runs them
+    ws = {n: workload_weights(wl, n) for n in ("Wq", "Wk", "Wv")}
+    Cs = [poisoned(T * ws[n][0].n, torch.float32, 0xFF).view(T, ws[n][0].n) for n in ws]
+    q8lib.q8_gemm_shared_multi([ws[n][0] for n in ws], pq, ps, T, Cs)
+    torch.cuda.synchronize()
+    for (n, (W, wq, wd)), C in zip(ws.items(), Cs):
+        Cn = to_np(C)
+        assert not np.isnan(Cn).any(), f"grouped gemm {n}: unwritten output cells"
+        pt, pn = sample_cells(T, W.n)
+        ref, norm = oracle.dot_pairs(wq, wd, qo, do, pt, pn)
+        assert_norm(Cn[pt, pn], ref, norm, 1e-5, f"grouped gemm {n} T={T}")
+    # and the separate launch of the largest member
+    W, wq, wd = ws["Wq"]
+    check_gemm_cells(W, wq, wd, qo, do, pq, ps, T, f"gemm Wq T={T}")
 
 
 def test_prefill_swiglu_full():

@@ -124,3 +124,32 @@ def test_gemm_scale_plane_two_byte_aligned(K):
     ref, norm = oracle.gemm(wq, wd, qo, do)
     assert_norm(to_np(C2), ref, norm, 1e-5, f"gemm 2-byte-aligned scales K={K}")
     assert torch.equal(C1, C2)
+
+
+@pytest.mark.parametrize("T,K,Ns", [(130, 3584, (3584, 512, 512)), (65, 288, (129, 1, 300, 0, 128)),
+                                    (64, 640, (40, 257, 128, 1, 3, 200, 64, 130))])
+def test_gemm_shared_multi_matches_separate_and_oracle(T, K, Ns):
+    """One grouped launch over several weight matrices equals the separate launches bit for bit, and
+    the oracle within the tolerance (members of any N, including 0; K/32 odd takes the register
+    form of the weight scales)."""
+    x = synth.normal((T, K), stream=5600 + K)
+    pq, ps, qo, do, _ = plane_act(x)
+    Ws, ref = [], []
+    for i, n in enumerate(Ns):
+        W, wq, wd = weights(synth.normal((max(n, 1), K), stream=5700 + i, std=0.02))
+        if n == 0:
+            W = q8lib.Q8Weights(W.qs[:0], W.d[:0])
+        Ws.append(W)
+        ref.append((wq[:n], wd[:n]))
+    ldcs = [n + 5 for n in Ns]
+    grouped = [poisoned((T + 1) * ld, torch.float32, 0xFF).view(T + 1, ld) for ld in ldcs]
+    q8lib.q8_gemm_shared_multi(Ws, pq, ps, T, grouped, ldcs)
+    separate = [run_gemm(W, pq, ps, T, ldc=ld, rows=T + 1) for W, ld in zip(Ws, ldcs)]
+    torch.cuda.synchronize()
+    for i, n in enumerate(Ns):
+        g, sep = to_np(grouped[i]), to_np(separate[i])
+        assert np.array_equal(g[:T, :n].view(np.uint32), sep[:T, :n].view(np.uint32)), f"member {i} N={n}"
+        assert np.all(np.isnan(g[:T, n:])) and np.all(np.isnan(g[T:, :])), f"member {i}: stray writes"
+        if n:
+            r, norm = oracle.gemm(ref[i][0], ref[i][1], qo, do)
+            assert_norm(g[:T, :n], r, norm, 1e-5, f"grouped member {i} N={n}")
