@@ -366,9 +366,15 @@ def bench_prefill_swiglu(D, reps):
     b = swiglu_bytes(T, K, 1)
     out["swiglu_quant_plane64"] = {**t, "bytes": b, "GBps": b / t["mean_us"] / 1e3,
                                    "frac_hbm": b / t["mean_us"] / 1e3 / HBM_PEAK_GBS}
+    # plane only (y = NULL): for a down projection that reads no f32 activation
+    t3 = stats(time_each(D, lambda i: q8.swiglu_quant(g, u, q8.LAYOUT_PLANE64, None, pq, ps, f32=False), reps))
+    b3 = b - T * K * 4
+    out["swiglu_quant_plane64_no_f32"] = {**t3, "bytes": b3, "GBps": b3 / t3["mean_us"] / 1e3,
+                                          "frac_hbm": b3 / t3["mean_us"] / 1e3 / HBM_PEAK_GBS}
     t2 = stats(time_each(D, lambda i: q8.q8_gemm(W, pq, ps, T, C), reps))
     out[f"q8_gemm_{N}x{K}"] = gemm_entry(t2, T, N, K)
     out["slice_tok_per_s"] = T / ((t["mean_us"] + t2["mean_us"]) * 1e-6)
+    out["slice_tok_per_s_no_f32"] = T / ((t3["mean_us"] + t2["mean_us"]) * 1e-6)
     return out
 
 

@@ -107,7 +107,10 @@ int q8_quantize(const float* x, int64_t rows, int64_t k, int layout, int8_t* qs,
  * y[t][j] = x[t][j] * (1/sqrt(mean_j x[t][j]^2 + eps)) * w[j], f32.
  * The quantized output is q8_quantize applied to the y this call writes,
  * bit for bit. qs == NULL and sd == NULL: f32 output only (then `layout` is
- * ignored); either both or neither may be NULL.
+ * ignored); either both or neither may be NULL. y == NULL (with qs and sd
+ * given): the quantized output only, bit-identical to the one a call with y
+ * writes, for consumers that read no f32 activation ([P2] s3.1, mode 2).
+ * y and qs both NULL: Q8_EINVAL.
  * x, y: [rows][K] f32 (16-byte aligned), w: [K] f32 (16-byte aligned).
  */
 int rmsnorm_quant(const float* x, const float* w, float eps, float* y, int64_t rows, int64_t k, int layout,
@@ -115,7 +118,8 @@ int rmsnorm_quant(const float* x, const float* w, float eps, float* y, int64_t r
 
 /*
  * Fused SwiGLU + quantize ([P2] s3.2): y = gate / (1 + e^-gate) * up, f32,
- * and the quantized y as in rmsnorm_quant (NULL qs and sd: f32 only).
+ * and the quantized y as in rmsnorm_quant (NULL qs and sd: f32 only; NULL y:
+ * the quantized output only, [P2] s3.1 mode 2).
  * gate, up, y: [rows][K] f32, 16-byte aligned.
  */
 int swiglu_quant(const float* gate, const float* up, float* y, int64_t rows, int64_t k, int layout, int8_t* qs,

@@ -103,7 +103,8 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
             o.y = v[u].y * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].y)) * w[u].y;
             o.z = v[u].z * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].z)) * w[u].z;
             o.w = v[u].w * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].w)) * w[u].w;
-            if (live[u]) *reinterpret_cast<float4*>(y + trow[u] * K + (int64_t)blk[u] * kQK + sub * 4) = o;
+            if (y != nullptr && live[u])  // y == NULL: quantized output only
+                *reinterpret_cast<float4*>(y + trow[u] * K + (int64_t)blk[u] * kQK + sub * 4) = o;
             v[u] = o;
         }
         if constexpr (D != kDstNone) {
@@ -168,7 +169,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, co
     const int n4 = K >> 2;
     const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x + (live ? t : 0) * K);
     const float4* __restrict__ w4 = reinterpret_cast<const float4*>(w);
-    float4* __restrict__ y4 = reinterpret_cast<float4*>(y + (live ? t : 0) * K);
+    // y == NULL: the quantized output only, no f32 row is written
+    float4* __restrict__ y4 = y != nullptr ? reinterpret_cast<float4*>(y + (live ? t : 0) * K) : nullptr;
 
     auto row_sum = [&](float ss) {
         ss = wave_sum(ss);
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, co
             o.y = v[k].y * scale * wv[k].y;
             o.z = v[k].z * scale * wv[k].z;
             o.w = v[k].w * scale * wv[k].w;
-            if (live && idx < n4) y4[idx] = o;
+            if (y4 != nullptr && live && idx < n4) y4[idx] = o;
             v[k] = o;  // zero for padded rows and past K
         }
         if constexpr (D != kDstNone) {
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, co
                 o.y = a.y * scale * wq.y;
                 o.z = a.z * scale * wq.z;
                 o.w = a.w * scale * wq.w;
-                y4[idx] = o;
+                if (y4 != nullptr) y4[idx] = o;
             }
             if constexpr (D != kDstNone) {
                 const int c = idx >> 3;
@@ -422,8 +424,9 @@ int swiglu_quant(const float* gate, const float* up, float* y, int64_t rows, int
                  uint32_t* sd, void* stream) {
     int rc = check_act_shape(rows, k);
     if (rc) return rc;
-    if (gate == nullptr || up == nullptr || y == nullptr) return Q8_EINVAL;
+    if (gate == nullptr || up == nullptr) return Q8_EINVAL;
     if ((rc = check_dst(layout, qs, sd, true))) return rc;
+    if (y == nullptr && qs == nullptr) return Q8_EINVAL;  // nothing to produce
     if (!q8h::aligned(gate, 16) || !q8h::aligned(up, 16) || !q8h::aligned(y, 16)) return Q8_EALIGN;
     return launch_elementwise<true>(gate, up, y, rows, k, layout, qs, sd, (hipStream_t)stream);
 }
@@ -432,8 +435,9 @@ int rmsnorm_quant(const float* x, const float* w, float eps, float* y, int64_t r
                   int8_t* qs, uint32_t* sd, void* stream) {
     int rc = check_act_shape(rows, k);
     if (rc) return rc;
-    if (x == nullptr || w == nullptr || y == nullptr) return Q8_EINVAL;
+    if (x == nullptr || w == nullptr) return Q8_EINVAL;
     if ((rc = check_dst(layout, qs, sd, true))) return rc;
+    if (y == nullptr && qs == nullptr) return Q8_EINVAL;  // nothing to produce
     if (!q8h::aligned(x, 16) || !q8h::aligned(w, 16) || !q8h::aligned(y, 16)) return Q8_EALIGN;
     const int64_t tpad = (qs == nullptr) ? rows : padded_rows(rows, layout);
     if (tpad == 0) return Q8_OK;

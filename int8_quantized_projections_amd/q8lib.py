@@ -162,9 +162,10 @@ def q8_quantize(x: torch.Tensor, layout: int = LAYOUT_ROW, qs=None, sd=None):
 
 
 def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float, layout: int = LAYOUT_ROW, y=None, qs=None, sd=None,
-                  quant: bool = True):
+                  quant: bool = True, f32: bool = True):
+    """f32=False passes y = NULL: only the quantized activation is written (returned y is None)."""
     rows, k = _rows_k(x)
-    if y is None:
+    if y is None and f32:
         y = torch.empty_like(x)
     if quant and qs is None:
         qs, sd = alloc_act(rows, k, layout, x.device)
@@ -176,9 +177,10 @@ def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float, layout: int = LA
 
 
 def swiglu_quant(gate: torch.Tensor, up: torch.Tensor, layout: int = LAYOUT_ROW, y=None, qs=None, sd=None,
-                 quant: bool = True):
+                 quant: bool = True, f32: bool = True):
+    """f32=False passes y = NULL: only the quantized activation is written (returned y is None)."""
     rows, k = _rows_k(gate)
-    if y is None:
+    if y is None and f32:
         y = torch.empty_like(gate)
     if quant and qs is None:
         qs, sd = alloc_act(rows, k, layout, gate.device)

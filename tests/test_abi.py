@@ -75,7 +75,11 @@ def test_quantize_and_producers_reject_before_launch(L):
     assert L.rmsnorm_quant(f, f, 1e-6, f, 4, 64, 0, f, None, None) == Q8_EINVAL
     assert L.rmsnorm_quant(f, None, 1e-6, f, 4, 64, 0, None, None, None) == Q8_EINVAL
     assert L.rmsnorm_quant(f, f + 4, 1e-6, f, 4, 64, 0, None, None, None) == Q8_EALIGN
-    assert L.swiglu_quant(f, f, None, 4, 64, 1, f, f, None) == Q8_EINVAL
+    # y = NULL is valid only with a quantized output (plane-only mode); neither: nothing to produce
+    assert L.swiglu_quant(f, f, None, 4, 64, 1, None, None, None) == Q8_EINVAL
+    assert L.rmsnorm_quant(f, f, 1e-6, None, 4, 64, 0, None, None, None) == Q8_EINVAL
+    assert L.swiglu_quant(f, f, None, 4, 64, 1, f, None, None) == Q8_EINVAL
+    assert L.rmsnorm_quant(f, f, 1e-6, None, 0, 64, 1, f, f, None) == Q8_OK  # zero rows: no-op
     assert L.swiglu_quant(f, f, f, 4, 96 + 1, 1, f, f, None) == Q8_ESHAPE
     # zero rows is a valid no-op (nothing to launch)
     assert L.q8_quantize(f, 0, 64, 1, f, f, None) == Q8_OK

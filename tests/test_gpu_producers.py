@@ -158,7 +158,11 @@ def _rms_case(rows, K, layout, stream):
     y2 = poisoned(rows * K, torch.float32).view(rows, K)
     q8lib.rmsnorm_quant(up(x), up(w), 1e-6, layout, y2, quant=False)
     q2, s2 = quantize_dev(y, rows, K, layout)
+    # plane only (y = NULL): nothing but the quantized output is written
+    q3, s3 = poisoned(nq, torch.int8), poisoned(ns // 4, torch.int32)
+    q8lib.rmsnorm_quant(up(x), up(w), 1e-6, layout, None, q3, s3, f32=False)
     torch.cuda.synchronize()
+    assert torch.equal(qs, q3) and torch.equal(sd, s3), "plane-only call differs from the call that writes y"
     return x, w, y, qs, sd, y2, q2, s2
 
 
@@ -185,7 +189,10 @@ def _swiglu_case(rows, K, layout, stream):
     y2 = poisoned(rows * K, torch.float32).view(rows, K)
     q8lib.swiglu_quant(up(g), up(u), layout, y2, quant=False)
     q2, s2 = quantize_dev(y, rows, K, layout)
+    q3, s3 = poisoned(nq, torch.int8), poisoned(ns // 4, torch.int32)
+    q8lib.swiglu_quant(up(g), up(u), layout, None, q3, s3, f32=False)
     torch.cuda.synchronize()
+    assert torch.equal(qs, q3) and torch.equal(sd, s3), "plane-only call differs from the call that writes y"
     return g, u, y, qs, sd, y2, q2, s2
 
 
