@@ -99,6 +99,11 @@ def gemv_bytes(N, K):
     return N * K + N * (K // 32) * 2 + K + (K // 32) * 4 + N * 4
 
 
+def gemv_f32_bytes(N, K):
+    """Algorithmic bytes of a GEMV on an f32 activation quantized in the launch."""
+    return N * K + N * (K // 32) * 2 + K * 4 + N * 4
+
+
 def quant_bytes(rows, K, layout=0):
     qrows = rows if layout == 0 else (rows + 63) // 64 * 64
     return rows * K * 4 + qrows * K + qrows * (K // 32) * 4
@@ -175,8 +180,7 @@ def decode_step_bytes():
     parts = {
         "rmsnorm_quant_row": rms_bytes(1, H),
         "q8_gemv_shared_multi_x6": grouped,
-        "q8_quantize_128": quant_bytes(1, 128),
-        "q8_gemv_4096x128": gemv_bytes(4096, 128),
+        "q8_gemv_f32_4096x128": gemv_f32_bytes(4096, 128),
     }
     return parts
 
@@ -205,8 +209,8 @@ def bench_decode(D, steps, warmup, log_reps):
             ("rmsnorm_quant_row", lambda: q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_ROW, y, aq, asd)),
             ("q8_gemv_shared_multi_x6", lambda: q8.q8_gemv_shared_multi(
                 [S[n] for n in DEC_GROUP], aq, asd, [outs[n] for n in DEC_GROUP])),
-            ("q8_quantize_128", lambda: q8.q8_quantize(x128, q8.LAYOUT_ROW, bq, bsd)),
-            ("q8_gemv_4096x128", lambda: q8.q8_gemv(S["W128"], bq, bsd, outs["W128"])),
+            # the K=128 activation has one consumer: quantized inside that GEMV's launch
+            ("q8_gemv_f32_4096x128", lambda: q8.q8_gemv_f32(S["W128"], x128.view(-1), outs["W128"])),
         ]
 
     def standalone(c):  # the same GEMVs as separate launches, for comparison
@@ -217,6 +221,8 @@ def bench_decode(D, steps, warmup, log_reps):
                 sum(gemv_bytes(DEC_N[n], H) for n in DEC_GROUP[:4]) - 3 * (H + (H // 32) * 4)),
             "q8_gemv_12288x7168": (lambda: q8.q8_gemv(S["W12288"], aq, asd, outs["W12288"]), gemv_bytes(12288, H)),
             "q8_gemv_96x7168": (lambda: q8.q8_gemv(S["W96"], aq, asd, outs["W96"]), gemv_bytes(96, H)),
+            "q8_quantize_128": (lambda: q8.q8_quantize(x128, q8.LAYOUT_ROW, bq, bsd), quant_bytes(1, 128)),
+            "q8_gemv_4096x128": (lambda: q8.q8_gemv(S["W128"], bq, bsd, outs["W128"]), gemv_bytes(4096, 128)),
         }
 
     def step(c):
@@ -286,6 +292,7 @@ def bench_gemv2048(D, reps):
     y = torch.empty(2048, device=D.dev)
     tq = stats(time_each(D, lambda i: q8.q8_quantize(x, q8.LAYOUT_ROW, aq, asd), reps))
     tg = stats(time_each(D, lambda i: q8.q8_gemv(Ws[i % n], aq, asd, y), reps))
+    tf = stats(time_each(D, lambda i: q8.q8_gemv_f32(Ws[i % n], x.view(-1), y), reps))
     # back-to-back replay of many distinct-weight GEMVs: aggregate bytes / aggregate time
     R = min(n, 200)
     g = torch.cuda.CUDAGraph()
@@ -301,7 +308,10 @@ def bench_gemv2048(D, reps):
     torch.cuda.synchronize()
     agg_us = e0.elapsed_time(e1) * 1e3 / R
     gb = gemv_bytes(2048, 2048)
+    fb = gemv_f32_bytes(2048, 2048)
     return {
+        "q8_gemv_f32_2048x2048": {**tf, "bytes": fb, "GBps": fb / tf["mean_us"] / 1e3,
+                                  "frac_hbm": fb / tf["mean_us"] / 1e3 / HBM_PEAK_GBS, "launches": 1},
         "q8_quantize_2048": {**tq, "bytes": quant_bytes(1, 2048), "GBps": quant_bytes(1, 2048) / tq["mean_us"] / 1e3},
         "q8_gemv_2048x2048": {**tg, "bytes": gb, "GBps": gb / tg["mean_us"] / 1e3,
                               "frac_hbm": gb / tg["mean_us"] / 1e3 / HBM_PEAK_GBS},
@@ -547,7 +557,7 @@ def main():
         "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": "decode_h7168", "batch": 1, "hidden": 7168,
                    "gemvs": "rmsnorm_quant ROW -> one grouped q8_gemv_shared_multi over N=4096/512/512/4096/"
-                            "12288/96 (K=7168); q8_quantize K=128 -> q8_gemv N=4096 K=128",
+                            "12288/96 (K=7168); q8_gemv_f32 N=4096 K=128 (its activation quantized in the launch)",
                    "launches_per_step": dec["launches_per_step"], "weight_copies": dec["copies"],
                    "timing": "HIP graph of all timed steps, HIP events around the replay"},
         "roofline": roofline,

@@ -136,6 +136,18 @@ int swiglu_quant(const float* gate, const float* up, float* y, int64_t rows, int
 int q8_gemv(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, float* y, void* stream);
 
 /*
+ * Batch-1 Q8_0 GEMV on an f32 activation, quantized inside the same launch
+ * ([P1] s3-s3.1: at decode a quantize launch costs far more than its bytes,
+ * so launches should be removed; for an activation with a single consumer the
+ * quantize moves into that consumer). x: [K] f32, 16-byte aligned, with
+ * K = W->k <= 8192 (Q8_ESHAPE otherwise; wider activations are quantized once
+ * with q8_quantize). Every wave quantizes the blocks it holds with the
+ * q8_quantize arithmetic, so y is bit-identical to q8_quantize(x) followed by
+ * q8_gemv(W, ...). y: [N] f32.
+ */
+int q8_gemv_f32(const q8_weights* W, const float* x, float* y, void* stream);
+
+/*
  * Several GEMVs that read the same activation, in one launch ([P1] s2.5,
  * s6: one activation feeding q/k/v/g, and the "more general grouped kernel"
  * for consumers of one activation at different N).

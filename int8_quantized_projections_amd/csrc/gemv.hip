@@ -22,6 +22,8 @@
 //    grouped launch give bit-identical outputs ([P1] s8 invariant).
 #include "q8_common.h"
 
+#include <type_traits>
+
 using namespace q8;
 
 namespace {
@@ -29,6 +31,7 @@ namespace {
 constexpr int kMaxMats = 8;
 constexpr int kWavesPerWg = 4;
 constexpr int kMaxWaves = 256 * 16;  // persistent grid cap: 256 CUs x 16 resident waves
+constexpr int64_t kMaxF32K = 8192;    // q8_gemv_f32: the activation fits one chunk (64 lanes x 4 blocks)
 
 struct GemvArgs {
     const int8_t* wq[kMaxMats];
@@ -69,10 +72,12 @@ __device__ __forceinline__ int dot32(const uint4& w0, const uint4& w1, const uin
 // (a chunk is W*NBL blocks; K wider than one chunk reloads the activation
 // chunk per row group). R: rows per lane group per iteration. MULTI: rows
 // are the concatenation of several matrices (the grouped launch); the
-// per-row arithmetic is the same code either way.
-template <int W, int NBL, int R, bool MULTI>
+// per-row arithmetic is the same code either way. F32A: the activation is
+// f32 (ax) and each lane quantizes the blocks it holds (one chunk only).
+template <int W, int NBL, int R, bool MULTI, bool F32A = false>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __restrict__ aq,
-                                              const uint32_t* __restrict__ asd, int K, int nb, int64_t groups) {
+                                              const uint32_t* __restrict__ asd, const float* __restrict__ ax, int K,
+                                              int nb, int64_t groups) {
     constexpr int G = kWave / W;  // row slots per wave
     constexpr int CH = W * NBL;   // blocks per chunk
     const int lane = threadIdx.x & (kWave - 1);
@@ -96,9 +101,24 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __res
             da[j] = f16_value(asd[bc]);
         }
     };
-    if (nchunks == 1) load_act(0);
+    // F32A (one chunk, K <= 8192): the f32 blocks are loaded before the first row
+    // group's weights and quantized after those weight loads are issued, so the
+    // two cold accesses overlap.
+    float4 xv[F32A ? NBL : 1][8];
+    if constexpr (F32A) {
+#pragma unroll
+        for (int j = 0; j < NBL; ++j) {
+            const int b = u + j * W;
+            const int bc = b < nb ? b : nb - 1;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xv[j][i] = *reinterpret_cast<const float4*>(ax + (int64_t)bc * kQK + 4 * i);
+        }
+    } else if (nchunks == 1) {
+        load_act(0);
+    }
 
-    for (int64_t gi = wave_id; gi < groups; gi += nwaves) {
+    // One row group; `first` (a compile-time flag) marks the wave's first group.
+    auto body = [&](int64_t gi, auto first) {
         const int8_t* wrow[R];
         const uint16_t* drow[R];
         float* yout[R];
@@ -130,8 +150,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __res
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 
-        for (int ch = 0; ch < nchunks; ++ch) {
-            if (nchunks > 1) load_act(ch);
+        const int nch = F32A ? 1 : nchunks;  // F32A: one chunk (a constant trip count keeps the order below)
+        for (int ch = 0; ch < nch; ++ch) {
+            if constexpr (!F32A)
+                if (nchunks > 1) load_act(ch);
             uint4 w0[R][NBL], w1[R][NBL];
             uint16_t dw[R][NBL];
             bool inb[NBL];
@@ -146,6 +168,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __res
                     w0[r][j] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK);
                     w1[r][j] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK + 16);
                     dw[r][j] = drow[r][bc];
+                }
+            }
+            if constexpr (F32A && decltype(first)::value) {
+                __builtin_amdgcn_sched_barrier(0);  // the weight loads above are issued before this waits on x
+#pragma unroll
+                for (int j = 0; j < NBL; ++j) {
+                    uint32_t dbits;
+                    quantize_lane32(xv[j], a0[j], a1[j], dbits);
+                    da[j] = f16_value(dbits);
                 }
             }
 #pragma unroll
@@ -164,7 +195,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __res
             const float v = group_sum<W>(acc[r]);
             if (u == 0 && valid[r]) *yout[r] = v;
         }
-    }
+    };
+    if (wave_id < groups) body(wave_id, std::true_type{});
+    for (int64_t gi = wave_id + nwaves; gi < groups; gi += nwaves) body(gi, std::false_type{});
 }
 
 struct Plan {
@@ -201,43 +234,44 @@ Plan make_plan(int64_t total, int nb, int force_rows) {
     return p;
 }
 
-template <int W, int NBL, bool MULTI>
+template <int W, int NBL, bool MULTI, bool F32A>
 void launch_r(const Plan& p, dim3 grid, hipStream_t s, const GemvArgs& a, const int8_t* aq, const uint32_t* asd,
-              int K, int nb) {
+              const float* ax, int K, int nb) {
     if (p.rows == 4)
-        hipLaunchKernelGGL((k_gemv<W, NBL, 4, MULTI>), grid, dim3(256), 0, s, a, aq, asd, K, nb, p.groups);
+        hipLaunchKernelGGL((k_gemv<W, NBL, 4, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
     else if (p.rows == 2)
-        hipLaunchKernelGGL((k_gemv<W, NBL, 2, MULTI>), grid, dim3(256), 0, s, a, aq, asd, K, nb, p.groups);
+        hipLaunchKernelGGL((k_gemv<W, NBL, 2, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
     else
-        hipLaunchKernelGGL((k_gemv<W, NBL, 1, MULTI>), grid, dim3(256), 0, s, a, aq, asd, K, nb, p.groups);
+        hipLaunchKernelGGL((k_gemv<W, NBL, 1, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
 }
 
-template <bool MULTI>
-void launch_m(const Plan& p, hipStream_t s, const GemvArgs& a, const int8_t* aq, const uint32_t* asd, int K, int nb) {
+template <bool MULTI, bool F32A>
+void launch_m(const Plan& p, hipStream_t s, const GemvArgs& a, const int8_t* aq, const uint32_t* asd, const float* ax,
+              int K, int nb) {
     const dim3 grid((unsigned)p.workgroups);
     switch (p.lanes) {
-        case 1: launch_r<1, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
-        case 2: launch_r<2, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
-        case 4: launch_r<4, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
-        case 8: launch_r<8, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
-        case 16: launch_r<16, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
-        case 32: launch_r<32, 1, MULTI>(p, grid, s, a, aq, asd, K, nb); break;
+        case 1: launch_r<1, 1, MULTI, F32A>(p, grid, s, a, aq, asd, ax, K, nb); break;
+        case 2: launch_r<2, 1, MULTI, F32A>(p, grid, s, a, aq, asd, ax, K, nb); break;
+        case 4: launch_r<4, 1, MULTI, F32A>(p, grid, s, a, aq, asd, ax, K, nb); break;
+        case 8: launch_r<8, 1, MULTI, F32A>(p, grid, s, a, aq, asd, ax, K, nb); break;
+        case 16: launch_r<16, 1, MULTI, F32A>(p, grid, s, a, aq, asd, ax, K, nb); break;
+        case 32: launch_r<32, 1, MULTI, F32A>(p, grid, s, a, aq, asd, ax, K, nb); break;
         default:
             if (p.nbl == 1)
-                launch_r<64, 1, MULTI>(p, grid, s, a, aq, asd, K, nb);
+                launch_r<64, 1, MULTI, F32A>(p, grid, s, a, aq, asd, ax, K, nb);
             else if (p.nbl == 2)
-                launch_r<64, 2, MULTI>(p, grid, s, a, aq, asd, K, nb);
+                launch_r<64, 2, MULTI, F32A>(p, grid, s, a, aq, asd, ax, K, nb);
             else
-                launch_r<64, 4, MULTI>(p, grid, s, a, aq, asd, K, nb);
+                launch_r<64, 4, MULTI, F32A>(p, grid, s, a, aq, asd, ax, K, nb);
     }
 }
 
 void launch(const Plan& p, bool multi, hipStream_t s, const GemvArgs& a, const int8_t* aq, const uint32_t* asd, int K,
             int nb) {
     if (multi)
-        launch_m<true>(p, s, a, aq, asd, K, nb);
+        launch_m<true, false>(p, s, a, aq, asd, nullptr, K, nb);
     else
-        launch_m<false>(p, s, a, aq, asd, K, nb);
+        launch_m<false, false>(p, s, a, aq, asd, nullptr, K, nb);
 }
 
 int check_weights(const q8_weights* w) {
@@ -321,6 +355,29 @@ int q8_gemv_shared_multi_ex(int m, const q8_weights* const* W, const int8_t* a_q
 int q8_gemv_shared_multi(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
                          float* const* y, void* stream) {
     return q8_gemv_shared_multi_ex(m, W, a_qs, a_sd, y, 0, stream);
+}
+
+int q8_gemv_f32(const q8_weights* W, const float* x, float* y, void* stream) {
+    int rc = check_weights(W);
+    if (rc) return rc;
+    if (W->k > kMaxF32K) return Q8_ESHAPE;
+    if (x == nullptr || (y == nullptr && W->n > 0)) return Q8_EINVAL;
+    if (!q8h::aligned(x, 16) || !q8h::aligned(y, 4)) return Q8_EALIGN;
+    if (W->n == 0) return Q8_OK;
+    GemvArgs a;
+    for (int i = 0; i < kMaxMats; ++i) {
+        a.wq[i] = W->qs;
+        a.wd[i] = W->d;
+        a.y[i] = y;
+        a.off[i] = i == 0 ? 0 : INT64_MAX;
+    }
+    a.total = W->n;
+    a.safe_q = W->qs;
+    a.safe_d = W->d;
+    const int nb = (int)(W->k / kQK);
+    const Plan p = make_plan(W->n, nb, 0);
+    launch_m<false, true>(p, (hipStream_t)stream, a, nullptr, nullptr, x, (int)W->k, nb);
+    return q8h::launch_status();
 }
 
 int q8_gemv(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, float* y, void* stream) {

@@ -154,13 +154,15 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
 // NV == 0: rows wider than the register budget; x is read twice (the second
 // read hits L2), with the same per-lane order of the sum of squares.
 // ---------------------------------------------------------------------------
-template <int D, int NV, int WPR>
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, const float* __restrict__ w, float eps,
-                                                 float* __restrict__ y, int64_t rows, int64_t tpad, int K, int nb,
-                                                 int8_t* __restrict__ qs, uint32_t* __restrict__ sd) {
-    constexpr int kRowsPerWg = kWavesPerWg / WPR;
+template <int D, int NV, int WPR, int WAVES = kWavesPerWg>
+__global__ __launch_bounds__(WAVES * 64) void k_rmsnorm(const float* __restrict__ x, const float* __restrict__ w,
+                                                        float eps, float* __restrict__ y, int64_t rows, int64_t tpad,
+                                                        int K, int nb, int8_t* __restrict__ qs,
+                                                        uint32_t* __restrict__ sd) {
+    static_assert(WAVES % WPR == 0, "whole rows per workgroup");
+    constexpr int kRowsPerWg = WAVES / WPR;
     constexpr int kStride = kWave * WPR;  // float4 stride between a lane's elements
-    __shared__ float part[kWavesPerWg];
+    __shared__ float part[WAVES];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = xcd_contiguous(blockIdx.x, gridDim.x) * kRowsPerWg + wave / WPR;
     const int li = (wave % WPR) * kWave + lane;  // lane index inside the row
@@ -332,24 +334,38 @@ int launch_elementwise(const float* a, const float* b, float* y, int64_t rows, i
     return q8h::launch_status();
 }
 
-template <int D, int WPR>
+template <int D, int WPR, int WAVES = kWavesPerWg>
 void launch_rms(int nv, dim3 grid, hipStream_t s, const float* x, const float* w, float eps, float* y, int64_t rows,
                 int64_t tpad, int k, int nb, int8_t* qs, uint32_t* sd) {
-#define Q8_RMS_CASE(N)                                                                                              \
-    case N:                                                                                                         \
-        hipLaunchKernelGGL((k_rmsnorm<D, N, WPR>), grid, dim3(256), 0, s, x, w, eps, y, rows, tpad, k, nb, qs, sd); \
+    const dim3 block(WAVES * 64);
+#define Q8_RMS_CASE(N)                                                                                           \
+    case N:                                                                                                      \
+        hipLaunchKernelGGL((k_rmsnorm<D, N, WPR, WAVES>), grid, block, 0, s, x, w, eps, y, rows, tpad, k, nb, qs, \
+                           sd);                                                                                  \
         break;
+    // at 1024 threads a lane has 128 VGPRs: more than 8 float4 per lane take the two-pass form
+    if (WAVES > kWavesPerWg && nv > 8) nv = 0;
     switch (nv) {
         Q8_RMS_CASE(1)
         Q8_RMS_CASE(2)
         Q8_RMS_CASE(4)
         Q8_RMS_CASE(8)
-        Q8_RMS_CASE(12)
-        Q8_RMS_CASE(16)
-        Q8_RMS_CASE(24)
-        Q8_RMS_CASE(32)
+        case 12:
+        case 16:
+        case 24:
+        case 32:
+            if constexpr (WAVES == kWavesPerWg) {
+                switch (nv) {
+                    Q8_RMS_CASE(12)
+                    Q8_RMS_CASE(16)
+                    Q8_RMS_CASE(24)
+                    Q8_RMS_CASE(32)
+                }
+                break;
+            }
+            [[fallthrough]];
         default:
-            hipLaunchKernelGGL((k_rmsnorm<D, 0, WPR>), grid, dim3(256), 0, s, x, w, eps, y, rows, tpad, k, nb, qs,
+            hipLaunchKernelGGL((k_rmsnorm<D, 0, WPR, WAVES>), grid, block, 0, s, x, w, eps, y, rows, tpad, k, nb, qs,
                                sd);
     }
 #undef Q8_RMS_CASE
@@ -365,16 +381,21 @@ int rms_nv(int64_t k, int wpr) {
     return 0;
 }
 
-// Waves per row: 4 when there are few rows (a decode row spreads over 256
-// lanes), else 2 (half the row per wave keeps the kernel near 100 VGPRs, so
-// enough waves are resident to stream).
-int rms_wpr(int64_t rows) { return rows < 1024 ? 4 : 2; }
+// Waves per row: 16 (one 1024-thread workgroup per row) for a handful of rows,
+// as at decode, where a row's latency is the cost: each lane then quantizes
+// two blocks instead of eight; 4 up to 1024 rows; else 2 (half the row per wave
+// keeps the kernel near 100 VGPRs, so enough waves are resident to stream).
+int rms_wpr(int64_t rows) { return rows <= 16 ? 16 : rows < 1024 ? 4 : 2; }
 
 template <int D>
 void dispatch_rms(hipStream_t s, const float* x, const float* w, float eps, float* y, int64_t rows, int64_t tpad,
                   int k, int nb, int8_t* qs, uint32_t* sd) {
     const int wpr = rms_wpr(rows);
     const int nv = rms_nv(k, wpr);
+    if (wpr == 16) {
+        launch_rms<D, 16, 16>(nv, dim3((unsigned)tpad), s, x, w, eps, y, rows, tpad, k, nb, qs, sd);
+        return;
+    }
     const dim3 grid((unsigned)q8h::ceil_div(tpad, kWavesPerWg / wpr));
     if (wpr == 4)
         launch_rms<D, 4>(nv, grid, s, x, w, eps, y, rows, tpad, k, nb, qs, sd);

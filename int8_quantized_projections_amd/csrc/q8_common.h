@@ -116,6 +116,48 @@ __device__ __forceinline__ Quant8 quantize_block8(float4 v) {
     return res;
 }
 
+// quantize_block8's arithmetic for a whole 32-value block held by one lane
+// (a consumer quantizing its own activation): the same bits. The IEEE division
+// is redone for all 32 values when any of them is near a half-integer; for the
+// others it gives the same integer as the reciprocal path. ssum is not formed.
+__device__ __forceinline__ void quantize_lane32(const float4 (&v)[8], uint4& q0, uint4& q1, uint32_t& dbits) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    const float d = a / 127.0f;
+    const float r = d != 0.0f ? __builtin_amdgcn_rcpf(d) : 0.0f;
+    float n[32];
+    int slow = (int)(d != 0.0f && d < 0x1p-126f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float z = x4[c] * r;
+            n[4 * i + c] = __builtin_rintf(z);
+            slow |= (int)near_half(z, n[4 * i + c]);
+        }
+    }
+    if (slow) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            n[4 * i + 0] = __builtin_rintf(v[i].x / d);
+            n[4 * i + 1] = __builtin_rintf(v[i].y / d);
+            n[4 * i + 2] = __builtin_rintf(v[i].z / d);
+            n[4 * i + 3] = __builtin_rintf(v[i].w / d);
+        }
+    }
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        w[i] = (uint32_t)(clamp127(n[4 * i]) & 0xFF) | ((uint32_t)(clamp127(n[4 * i + 1]) & 0xFF) << 8) |
+               ((uint32_t)(clamp127(n[4 * i + 2]) & 0xFF) << 16) | ((uint32_t)(clamp127(n[4 * i + 3]) & 0xFF) << 24);
+    q0 = make_uint4(w[0], w[1], w[2], w[3]);
+    q1 = make_uint4(w[4], w[5], w[6], w[7]);
+    dbits = f16_bits(d);
+}
+
 // Workgroups are dealt to the 8 XCDs in turn (workgroup p runs on XCD p % 8).
 // Remap a linear workgroup index so that each XCD gets one contiguous range
 // of logical indices (the first count % 8 XCDs one more than the others):

@@ -54,6 +54,7 @@ def lib() -> ctypes.CDLL:
             "rmsnorm_quant": ([vp, vp, ctypes.c_float, vp, i64, i64, ci, vp, vp, vp], ci),
             "swiglu_quant": ([vp, vp, vp, i64, i64, ci, vp, vp, vp], ci),
             "q8_gemv": ([wp, vp, vp, vp, vp], ci),
+            "q8_gemv_f32": ([wp, vp, vp, vp], ci),
             "q8_gemv_shared_multi": ([ci, ctypes.POINTER(wp), vp, vp, ctypes.POINTER(vp), vp], ci),
             "q8_gemv_shared_multi_ex": ([ci, ctypes.POINTER(wp), vp, vp, ctypes.POINTER(vp), ci, vp], ci),
             "q8_gemv_plan": ([i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(i64)], ci),
@@ -199,6 +200,15 @@ def q8_gemv(W: Q8Weights, a_qs: torch.Tensor, a_sd: torch.Tensor, y=None) -> tor
         y = torch.empty(W.n, dtype=torch.float32, device=a_qs.device)
     ws = W.struct()
     _check(lib().q8_gemv(ctypes.byref(ws), _ptr(a_qs), _ptr(a_sd), _ptr(y), _stream(a_qs.device)), "q8_gemv")
+    return y
+
+
+def q8_gemv_f32(W: Q8Weights, x: torch.Tensor, y=None) -> torch.Tensor:
+    """GEMV on an f32 activation [K] quantized inside the launch (K <= 8192)."""
+    if y is None:
+        y = torch.empty(W.n, dtype=torch.float32, device=x.device)
+    ws = W.struct()
+    _check(lib().q8_gemv_f32(ctypes.byref(ws), _ptr(x), _ptr(y), _stream(x.device)), "q8_gemv_f32")
     return y
 
 

@@ -101,6 +101,12 @@ def test_gemv_and_gemm_reject_before_launch(L):
     assert L.q8_gemv(ctypes.byref(w), f + 4, f, f, None) == Q8_EALIGN
     assert L.q8_gemv(ctypes.byref(w), f, f, f + 2, None) == Q8_EALIGN
     assert L.q8_gemv(ctypes.byref(_w(0, 64)), f, f, f, None) == Q8_OK  # N = 0: no-op
+    # gemv on an f32 activation: K <= 8192, x 16-byte aligned
+    assert L.q8_gemv_f32(ctypes.byref(_w(8, 8192 + 32)), f, f, None) == Q8_ESHAPE
+    assert L.q8_gemv_f32(ctypes.byref(w), None, f, None) == Q8_EINVAL
+    assert L.q8_gemv_f32(ctypes.byref(w), f + 4, f, None) == Q8_EALIGN
+    assert L.q8_gemv_f32(ctypes.byref(w), f, None, None) == Q8_EINVAL
+    assert L.q8_gemv_f32(ctypes.byref(_w(0, 64)), f, f, None) == Q8_OK  # N = 0: no-op
     # grouped: m range, K must agree
     ws = (ctypes.POINTER(q8lib._Weights) * 2)(ctypes.pointer(_w(8, 64)), ctypes.pointer(_w(8, 96)))
     ys = (ctypes.c_void_p * 2)(f, f)

@@ -63,7 +63,9 @@ def test_gemv_2048_full():
     W, wq, wd = workload_weights(wl, "W")
     qs, sd = q8lib.q8_quantize(up(x), ROW)
     y = q8lib.q8_gemv(W, qs, sd)
+    yf = q8lib.q8_gemv_f32(W, up(x).view(-1))
     torch.cuda.synchronize()
+    assert torch.equal(yf, y), "q8_gemv_f32 differs from q8_quantize + q8_gemv"
     qo, do, so = oracle.quantize(x)
     assert np.array_equal(to_np(qs), qo.reshape(-1))
     assert np.array_equal(to_np(sd).view(np.uint32), oracle.pack_sd(do, so).reshape(-1))
@@ -88,6 +90,7 @@ def test_decode_projection_set_full():
     W128, wq128, wd128 = workload_weights(wl, "W128")
     bq, bsd = q8lib.q8_quantize(up(x128), ROW)
     y128 = q8lib.q8_gemv(W128, bq, bsd)
+    y128f = q8lib.q8_gemv_f32(W128, up(x128).view(-1))  # as the benchmark's step runs it
     torch.cuda.synchronize()
     assert_rel(to_np(y), y_ref, 1e-5, "rmsnorm 1x7168")
     assert torch.equal(aq_f, aq2) and torch.equal(asd_f, asd2), "fused quantize differs from standalone"
@@ -100,6 +103,8 @@ def test_decode_projection_set_full():
     assert np.array_equal(to_np(bq), q1.reshape(-1))
     ref, norm = oracle.gemv(wq128, wd128, q1[0], d1[0])
     assert_norm(to_np(y128), ref, norm, 1e-5, "gemv 4096x128")
+    assert torch.equal(y128f, y128), "q8_gemv_f32 differs from q8_quantize + q8_gemv"
+    assert_norm(to_np(y128f), ref, norm, 1e-5, "gemv_f32 4096x128")
 
 
 def test_prefill_rms_full():

@@ -155,3 +155,47 @@ def test_gemv_deterministic():
     b = run_gemv(W, aq, asd)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def edge_activation(K, seed):
+    """A K-wide activation made of quantize edge cases: exact ties on power-of-two
+    scales, one ulp either side of half-integers, zero blocks, f16- and
+    f32-subnormal scales, and random blocks over many magnitudes."""
+    rng = np.random.default_rng(seed)
+    blocks = []
+    while sum(b.size for b in blocks) < K:
+        kind = len(blocks) % 6
+        if kind == 0:
+            m = rng.integers(-126, 127, size=32) + 0.5
+            m[0] = 127.0
+            blocks.append(m * 2.0 ** int(rng.integers(-8, 4)))
+        elif kind in (1, 2):
+            base = (rng.integers(-120, 121, size=32) + 0.5).astype(np.float32)
+            base[0] = 127.0
+            blocks.append(np.nextafter(base, np.float32(np.inf if kind == 1 else -np.inf)))
+        elif kind == 3:
+            blocks.append(np.zeros(32) if rng.integers(2) else rng.standard_normal(32) * 1e-40)
+        elif kind == 4:
+            blocks.append(rng.standard_normal(32) * 1e-6)
+        else:
+            blocks.append(rng.standard_normal(32) * 2.0 ** int(rng.integers(-20, 12)))
+    return np.concatenate(blocks)[:K].astype(np.float32).reshape(1, K)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (7, 96), (4096, 128), (300, 1024), (2048, 2048), (129, 2080),
+                                 (1025, 4096), (65, 7168), (300, 8192)])
+def test_gemv_f32_equals_quantize_then_gemv(N, K):
+    """q8_gemv_f32 quantizes inside the launch: the same bits as q8_quantize + q8_gemv,
+    on Gaussian and on quantize-edge-case activations; and the oracle's value."""
+    W, wq, wd = weights(synth.normal((N, K), stream=4600 + N, std=0.02))
+    for x in (synth.normal((1, K), stream=4601 + K), edge_activation(K, K)):
+        xd = up(x)
+        aq, asd = q8lib.q8_quantize(xd, q8lib.LAYOUT_ROW)
+        y_ref = run_gemv(W, aq, asd)
+        y = poisoned(N, torch.float32, 0xFF)
+        q8lib.q8_gemv_f32(W, xd.view(-1), y)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32)), f"q8_gemv_f32 {N}x{K}"
+        qo, do, _ = oracle.quantize(x)
+        ref, norm = oracle.gemv(wq, wd, qo[0], do[0])
+        assert_norm(to_np(y), ref, norm, 1e-5, f"q8_gemv_f32 {N}x{K} vs oracle")

@@ -166,8 +166,11 @@ def _rms_case(rows, K, layout, stream):
     return x, w, y, qs, sd, y2, q2, s2
 
 
+# rows <= 16 run one 1024-thread workgroup per row (K/4 > 8192 float4: the two-pass form), more rows 4 or 2
+# waves per row
 @pytest.mark.parametrize("rows,K,layout", [(1, 7168, ROW), (1, 3584, ROW), (3, 640, ROW), (70, 896, PLANE),
-                                           (130, 3584, PLANE), (64, 256, PLANE), (3, 9216, ROW), (65, 18944, PLANE)])
+                                           (130, 3584, PLANE), (64, 256, PLANE), (3, 9216, ROW), (65, 18944, PLANE),
+                                           (2, 40960, ROW), (16, 2048, PLANE), (17, 2048, PLANE), (1, 32, ROW)])
 def test_rmsnorm_quant(rows, K, layout):
     x, w, y, qs, sd, y2, q2, s2 = _rms_case(rows, K, layout, 3400 + K + rows)
     ref = oracle.rmsnorm_f64(x, w, 1e-6)
