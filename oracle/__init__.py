@@ -63,6 +63,11 @@ def lib():
             "q8o_gemm_full": ([vp, vp, i64, i64, vp, vp, i64, vp, vp], None),
             "q8o_block_isums": ([vp, i64, i64, vp, i64, vp], None),
             "q8o_num_threads": ([], ctypes.c_int),
+            "q4ko_scale_min": ([vp, ctypes.c_int, vp, vp], None),
+            "q4ko_decode": ([vp, i64, i64, vp, vp, vp, vp, vp], None),
+            "q4ko_dequant_f64": ([vp, i64, i64, vp], None),
+            "q4ko_dot_pairs": ([vp, i64, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp], None),
+            "q4ko_gemm_full": ([vp, i64, i64, vp, vp, vp, i64, vp, vp], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -275,3 +280,71 @@ def block_isums(wq, aq) -> np.ndarray:
     out = np.empty((T, N, K // QK), dtype=np.int32)
     lib().q8o_block_isums(wq.ctypes.data, N, K, aq.ctypes.data, T, out.ctypes.data)
     return out
+
+
+# -- q4_K weights --------------------------------------------------------------------
+Q4K_BLOCK = 144   # bytes per 256-value super-block
+Q4K_VALUES = 256
+
+
+def q4k_scale_min(scale_bytes, s: int):
+    """(sc, m) of sub-block s from the 12 packed scale bytes."""
+    b = _c(np.asarray(scale_bytes, dtype=np.uint8).reshape(12), np.uint8)
+    sc, m = ctypes.c_int(), ctypes.c_int()
+    lib().q4ko_scale_min(b.ctypes.data, s, ctypes.byref(sc), ctypes.byref(m))
+    return sc.value, m.value
+
+
+def q4k_decode(blocks, N: int, K: int):
+    """nib [N,K] u8, d and dmin [N,K/256] f16 bits, sc and m [N,K/32] u8."""
+    blocks = _c(blocks, np.uint8)
+    assert blocks.size == N * (K // Q4K_VALUES) * Q4K_BLOCK
+    nib = np.empty((N, K), np.uint8)
+    d = np.empty((N, K // Q4K_VALUES), np.uint16)
+    dmin = np.empty_like(d)
+    sc = np.empty((N, K // QK), np.uint8)
+    mn = np.empty_like(sc)
+    lib().q4ko_decode(blocks.ctypes.data, N, K, nib.ctypes.data, d.ctypes.data, dmin.ctypes.data, sc.ctypes.data,
+                      mn.ctypes.data)
+    return nib, d, dmin, sc, mn
+
+
+def q4k_dequant(blocks, N: int, K: int) -> np.ndarray:
+    """Element values [N, K] in f64."""
+    blocks = _c(blocks, np.uint8)
+    w = np.empty((N, K), np.float64)
+    lib().q4ko_dequant_f64(blocks.ctypes.data, N, K, w.ctypes.data)
+    return w
+
+
+def _q4k_args(blocks, N, K, aq, ad, assum):
+    blocks = _c(blocks, np.uint8)
+    assert blocks.size == N * (K // Q4K_VALUES) * Q4K_BLOCK
+    aq, ad, assum = _c(aq, np.int8), _c(ad, np.uint16), _c(assum, np.int16)
+    if aq.ndim == 1:
+        aq, ad, assum = aq.reshape(1, -1), ad.reshape(1, -1), assum.reshape(1, -1)
+    return blocks, aq, ad, assum
+
+
+def q4k_dot_pairs(blocks, N, K, aq, ad, assum, pt, pn):
+    """Reference (f64) and norm of cells (pt[i], pn[i]) for q4_K weights and q8_0 activations."""
+    blocks, aq, ad, assum = _q4k_args(blocks, N, K, aq, ad, assum)
+    T = aq.shape[0]
+    pt, pn = _c(pt, np.int64), _c(pn, np.int64)
+    assert np.all((pt >= 0) & (pt < T)) and np.all((pn >= 0) & (pn < N))
+    ref = np.empty(pt.size, np.float64)
+    norm = np.empty(pt.size, np.float64)
+    lib().q4ko_dot_pairs(blocks.ctypes.data, N, K, aq.ctypes.data, ad.ctypes.data, assum.ctypes.data, T,
+                         pt.ctypes.data, pn.ctypes.data, pt.size, ref.ctypes.data, norm.ctypes.data)
+    return ref, norm
+
+
+def q4k_gemm(blocks, N, K, aq, ad, assum):
+    """C_ref [T, N] and norm [T, N] for q4_K weights and q8_0 activations."""
+    blocks, aq, ad, assum = _q4k_args(blocks, N, K, aq, ad, assum)
+    T = aq.shape[0]
+    ref = np.empty((T, N), np.float64)
+    norm = np.empty((T, N), np.float64)
+    lib().q4ko_gemm_full(blocks.ctypes.data, N, K, aq.ctypes.data, ad.ctypes.data, assum.ctypes.data, T,
+                         ref.ctypes.data, norm.ctypes.data)
+    return ref, norm

@@ -315,3 +315,136 @@ void q8o_block_isums(const int8_t* wq, int64_t N, int64_t K, const int8_t* aq, i
         }
     }
 }
+
+/* ------------------------------------------------------------------------
+ * q4_K weights ([P3] s2, "the dequant-at-mma-time principle", and spec point
+ * 1): a super-block of 256 values in 144 bytes -- f16 d at +0, f16 dmin at +2,
+ * 12 bytes of packed 6-bit sub-block scales and mins at +4, 128 bytes of
+ * 4-bit values at +16. Sub-block s (values 32s..32s+31, s = 0..7) takes value
+ * j from byte 16 + 32*(s/2) + j: its low nibble for even s, its high nibble
+ * for odd s ([P3] s3.2, the listing's unpack). The value is
+ *   w = d * sc_s * nib - dmin * m_s          (nib unsigned, 0..15)
+ * ([P3] s3.2: "value = d*s*nib - dmin*m").
+ * The pages call the 6-bit decode get_scale_min_k4 without its bit layout;
+ * the GGUF q4_K layout is taken: with b the 12 bytes,
+ *   s < 4 : sc = b[s] & 63,                     m = b[s+4] & 63
+ *   s >= 4: sc = (b[s+4] & 15) | (b[s-4] >> 6) << 4,
+ *           m  = (b[s+4] >> 4) | (b[s]   >> 6) << 4.
+ * ---------------------------------------------------------------------- */
+#define QK_K 256
+#define Q4K_BYTES 144
+
+void q4ko_scale_min(const uint8_t* b, int s, int* sc, int* m) {
+    if (s < 4) {
+        *sc = b[s] & 63;
+        *m = b[s + 4] & 63;
+    } else {
+        *sc = (b[s + 4] & 15) | ((b[s - 4] >> 6) << 4);
+        *m = (b[s + 4] >> 4) | ((b[s] >> 6) << 4);
+    }
+}
+
+static int q4k_nibble(const uint8_t* blk, int s, int j) {
+    uint8_t byte = blk[16 + 32 * (s / 2) + j];
+    return (s % 2 == 0) ? (byte & 15) : (byte >> 4);
+}
+
+/* Decoded fields of [N][K/256] super-blocks: nib [N][K], d and dmin [N][K/256]
+ * (f16 bits), sc and mn [N][K/32]. */
+void q4ko_decode(const uint8_t* blocks, int64_t N, int64_t K, uint8_t* nib, uint16_t* d, uint16_t* dmin,
+                 uint8_t* sc, uint8_t* mn) {
+    int64_t nsb = K / QK_K;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t sb = 0; sb < nsb; ++sb) {
+            const uint8_t* blk = blocks + (n * nsb + sb) * Q4K_BYTES;
+            memcpy(&d[n * nsb + sb], blk, 2);
+            memcpy(&dmin[n * nsb + sb], blk + 2, 2);
+            for (int s = 0; s < 8; ++s) {
+                int a, b;
+                q4ko_scale_min(blk + 4, s, &a, &b);
+                sc[n * (K / QK) + sb * 8 + s] = (uint8_t)a;
+                mn[n * (K / QK) + sb * 8 + s] = (uint8_t)b;
+                for (int j = 0; j < QK; ++j) nib[n * K + sb * QK_K + s * QK + j] = (uint8_t)q4k_nibble(blk, s, j);
+            }
+        }
+    }
+}
+
+/* Element values w [N][K] in f64 (each exact: 11 + 6 + 4 bits, and 11 + 6 bits). */
+void q4ko_dequant_f64(const uint8_t* blocks, int64_t N, int64_t K, double* w) {
+    int64_t nsb = K / QK_K;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t sb = 0; sb < nsb; ++sb) {
+            const uint8_t* blk = blocks + (n * nsb + sb) * Q4K_BYTES;
+            uint16_t dh, mh;
+            memcpy(&dh, blk, 2);
+            memcpy(&mh, blk + 2, 2);
+            double dd = q8o_f16_to_f32(dh), dm = q8o_f16_to_f32(mh);
+            for (int s = 0; s < 8; ++s) {
+                int a, b;
+                q4ko_scale_min(blk + 4, s, &a, &b);
+                for (int j = 0; j < QK; ++j)
+                    w[n * K + sb * QK_K + s * QK + j] = dd * a * q4k_nibble(blk, s, j) - dm * b;
+            }
+        }
+    }
+}
+
+/* One output cell against a q8_0 activation row (values aq, f16 scales ad,
+ * block sums assum). Per 32-value sub-block b ([P2] s2.1: ssum is kept for the
+ * min-term correction):
+ *   isum_b = sum_j nib[32b+j] * qa[32b+j]                      (exact int32)
+ *   term_b = f16(da_b) * (f16(d) * sc_b * isum_b - f16(dmin) * m_b * ssum_b)
+ * which equals sum_j w_j * da_b * qa_j exactly. Each product is exact in f64;
+ * only the sum over b rounds. norm sums the absolute values of both parts. */
+static void q4k_dot_one(const uint8_t* row, int64_t K, const int8_t* aq, const uint16_t* ad, const int16_t* assum,
+                        double* ref, double* norm) {
+    int64_t nsb = K / QK_K;
+    double s = 0.0, a = 0.0;
+    for (int64_t sb = 0; sb < nsb; ++sb) {
+        const uint8_t* blk = row + sb * Q4K_BYTES;
+        uint16_t dh, mh;
+        memcpy(&dh, blk, 2);
+        memcpy(&mh, blk + 2, 2);
+        double dd = q8o_f16_to_f32(dh), dm = q8o_f16_to_f32(mh);
+        for (int sub = 0; sub < 8; ++sub) {
+            int64_t b = sb * 8 + sub;
+            int sc, m;
+            q4ko_scale_min(blk + 4, sub, &sc, &m);
+            int32_t is = 0;
+            for (int j = 0; j < QK; ++j) is += (int32_t)q4k_nibble(blk, sub, j) * (int32_t)aq[b * QK + j];
+            double da = q8o_f16_to_f32(ad[b]);
+            double t1 = da * dd * sc * (double)is;
+            double t2 = da * dm * m * (double)assum[b];
+            s += t1 - t2;
+            a += fabs(t1) + fabs(t2);
+        }
+    }
+    *ref = s;
+    *norm = a;
+}
+
+void q4ko_dot_pairs(const uint8_t* blocks, int64_t N, int64_t K, const int8_t* aq, const uint16_t* ad,
+                    const int16_t* assum, int64_t T, const int64_t* pt, const int64_t* pn, int64_t npairs,
+                    double* ref, double* norm) {
+    (void)N;
+    (void)T;
+    int64_t nb = K / QK, rowbytes = (K / QK_K) * Q4K_BYTES;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < npairs; ++i) {
+        int64_t t = pt[i], n = pn[i];
+        q4k_dot_one(blocks + n * rowbytes, K, aq + t * K, ad + t * nb, assum + t * nb, ref + i, norm + i);
+    }
+}
+
+void q4ko_gemm_full(const uint8_t* blocks, int64_t N, int64_t K, const int8_t* aq, const uint16_t* ad,
+                    const int16_t* assum, int64_t T, double* ref, double* norm) {
+    int64_t nb = K / QK, rowbytes = (K / QK_K) * Q4K_BYTES;
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t n = 0; n < N; ++n) {
+            q4k_dot_one(blocks + n * rowbytes, K, aq + t * K, ad + t * nb, assum + t * nb, ref + t * N + n,
+                        norm + t * N + n);
+        }
+    }
+}

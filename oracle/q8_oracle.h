@@ -59,6 +59,17 @@ void q8o_gemm_full(const int8_t* wq, const uint16_t* wd, int64_t N, int64_t K, c
                    const uint16_t* ad, int64_t T, double* ref, double* norm);
 void q8o_block_isums(const int8_t* wq, int64_t N, int64_t K, const int8_t* aq, int64_t T, int32_t* isum);
 
+/* q4_K weights (256-value super-blocks of 144 bytes) against q8_0 activations. */
+void q4ko_scale_min(const uint8_t* b, int s, int* sc, int* m);
+void q4ko_decode(const uint8_t* blocks, int64_t N, int64_t K, uint8_t* nib, uint16_t* d, uint16_t* dmin,
+                 uint8_t* sc, uint8_t* mn);
+void q4ko_dequant_f64(const uint8_t* blocks, int64_t N, int64_t K, double* w);
+void q4ko_dot_pairs(const uint8_t* blocks, int64_t N, int64_t K, const int8_t* aq, const uint16_t* ad,
+                    const int16_t* assum, int64_t T, const int64_t* pt, const int64_t* pn, int64_t npairs,
+                    double* ref, double* norm);
+void q4ko_gemm_full(const uint8_t* blocks, int64_t N, int64_t K, const int8_t* aq, const uint16_t* ad,
+                    const int16_t* assum, int64_t T, double* ref, double* norm);
+
 int q8o_num_threads(void);
 
 #ifdef __cplusplus

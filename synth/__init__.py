@@ -58,6 +58,8 @@ def lib():
         L.synth_uniform_f32.restype = None
         L.synth_uniform_i8.argtypes = [u64, u64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
         L.synth_uniform_i8.restype = None
+        L.synth_bytes.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        L.synth_bytes.restype = None
         _lib = L
     return _lib
 
@@ -84,6 +86,30 @@ def uniform_i8(shape, stream: int, lo: int, hi: int, seed: int = SEED, offset: i
     a = np.empty(n, dtype=np.int8)
     lib().synth_uniform_i8(seed, stream, offset, n, lo, hi, a.ctypes.data)
     return a.reshape(shape)
+
+
+def random_bytes(n: int, stream: int, seed: int = SEED, offset: int = 0) -> np.ndarray:
+    a = np.empty(n, dtype=np.uint8)
+    lib().synth_bytes(seed, stream, offset, n, a.ctypes.data)
+    return a
+
+
+def q4k_blocks(N: int, K: int, stream: int, d_exp: int = 2, dmin_exp: int = 5, seed: int = SEED,
+               row0: int = 0) -> np.ndarray:
+    """q4_K weights [N, K/256 * 144] as raw bytes, rows row0 .. row0+N-1 of the stream: every byte is random
+    except the two f16 fields of each 144-byte super-block, whose bit patterns get exponent field d_exp (d)
+    and dmin_exp (dmin) with a random 10-bit fraction (d in [2^-13, 2^-12), dmin in [2^-10, 2^-9) by
+    default). Any byte pattern is a valid block, so no encoding arithmetic is involved."""
+    nsb = K // 256
+    rowb = nsb * 144
+    raw = random_bytes(N * rowb, stream, seed, offset=row0 * rowb).reshape(N, nsb, 144)
+    d = raw[:, :, 0].astype(np.uint16) | ((raw[:, :, 1].astype(np.uint16) & 0x03) << 8) | (d_exp << 10)
+    m = raw[:, :, 2].astype(np.uint16) | ((raw[:, :, 3].astype(np.uint16) & 0x03) << 8) | (dmin_exp << 10)
+    raw[:, :, 0] = (d & 0xFF).astype(np.uint8)
+    raw[:, :, 1] = (d >> 8).astype(np.uint8)
+    raw[:, :, 2] = (m & 0xFF).astype(np.uint8)
+    raw[:, :, 3] = (m >> 8).astype(np.uint8)
+    return raw.reshape(N, rowb)
 
 
 # ---------------------------------------------------------------------------
@@ -148,6 +174,20 @@ WORKLOADS = {
         },
     },
 }
+
+
+# q4_K weight tensors (raw 144-byte super-blocks): (N, K), stream
+Q4K_WEIGHTS = {
+    # 6: prefill with q4_K weights: the rms-class plane (T=3325, d=3584) feeding the FFN gate and up
+    #    projections N=18944 K=3584 (the q4_K GEMM the pages measure)
+    "prefill_q4k": {"Wg": ((18944, 3584), 601), "Wu": ((18944, 3584), 602)},
+}
+
+
+def q4k_tensor(workload: str, name: str, rows: slice | None = None) -> np.ndarray:
+    (N, K), stream = Q4K_WEIGHTS[workload][name]
+    r0, r1 = (0, N) if rows is None else (rows.start or 0, N if rows.stop is None else rows.stop)
+    return q4k_blocks(r1 - r0, K, stream, row0=r0)
 
 
 def tensor(workload: str, name: str, rows: slice | None = None) -> np.ndarray:

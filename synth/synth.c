@@ -82,3 +82,8 @@ void synth_uniform_i8(uint64_t seed, uint64_t stream, int64_t offset, int64_t n,
         out[j] = (int8_t)v;
     }
 }
+
+/* n pseudo-random bytes: byte i is the low byte of draw offset+i of the stream. */
+void synth_bytes(uint64_t seed, uint64_t stream, int64_t offset, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)(synth_bits(seed, stream, (uint64_t)(offset + i)) & 0xFF);
+}

@@ -385,3 +385,104 @@ def test_generator_moments_and_offsets():
     assert np.array_equal(part, z[5000:6000])
     i8 = synth.uniform_i8((1 << 16,), stream=8, lo=-15, hi=15)
     assert i8.min() == -15 and i8.max() == 15
+
+
+# -- q4_K weights ([P3] s2-s3: 144-byte super-blocks, w = d*sc*nib - dmin*m) -----------------------
+Q4K_SCALE_BYTES = [0xC1, 0x02, 0x83, 0x44, 0x05, 0x46, 0x87, 0xC8, 0x21, 0x43, 0x65, 0x87]
+# (sc, m) of sub-blocks 0..7 for the bytes above, worked out by hand from the 6-bit layout:
+# s < 4 takes the low six bits of bytes s and s+4; s >= 4 takes the nibbles of byte s+4 and the
+# top two bits of bytes s-4 (scale) and s (min) as bits 4..5.
+Q4K_SCALE_EXPECT = [(1, 5), (2, 6), (3, 7), (4, 8), (49, 2), (3, 20), (37, 38), (23, 56)]
+
+
+def test_q4k_scale_min_worked_example():
+    for s, expect in enumerate(Q4K_SCALE_EXPECT):
+        assert oracle.q4k_scale_min(Q4K_SCALE_BYTES, s) == expect, s
+
+
+def test_q4k_scale_packing_uses_every_bit_once():
+    """Flipping any one of the 96 bits changes exactly one of the 16 six-bit fields, by a power of
+    two: the packing is a bijection between 12 bytes and 8 (scale, min) pairs."""
+    rng = np.random.default_rng(11)
+    base = rng.integers(0, 256, 12).astype(np.uint8)
+    fields = lambda b: [v for s in range(8) for v in oracle.q4k_scale_min(b, s)]
+    f0 = fields(base)
+    assert all(0 <= v < 64 for v in f0)
+    hit = set()
+    for bit in range(96):
+        b = base.copy()
+        b[bit // 8] ^= np.uint8(1 << (bit % 8))
+        diff = [(i, abs(a - c)) for i, (a, c) in enumerate(zip(f0, fields(b))) if a != c]
+        assert len(diff) == 1 and diff[0][1] in (1, 2, 4, 8, 16, 32), (bit, diff)
+        hit.add((diff[0][0], diff[0][1]))
+    assert len(hit) == 96  # each (field, bit) pair is reached by exactly one byte bit
+
+
+def _q4k_worked_block():
+    blk = np.zeros(144, np.uint8)
+    blk[0:2] = [0x00, 0x3C]  # d = 1.0
+    blk[2:4] = [0x00, 0x38]  # dmin = 0.5
+    blk[4:16] = Q4K_SCALE_BYTES
+    blk[16:] = np.arange(128, dtype=np.uint8)  # value byte i = i
+    return blk
+
+
+def test_q4k_values_worked_example():
+    """Values of a hand-made block (d = 1, dmin = 0.5, value bytes 0..127), worked out by hand:
+    sub-block s, value j reads byte 32*(s//2) + j, low nibble for even s, high for odd s."""
+    w = oracle.q4k_dequant(_q4k_worked_block(), 1, 256)[0]
+    cases = {  # (s, j): d*sc*nib - dmin*m
+        (0, 5): 1 * 5 - 0.5 * 5,      # byte 5, low nibble 5
+        (1, 5): 2 * 0 - 0.5 * 6,      # byte 5, high nibble 0
+        (3, 31): 4 * 3 - 0.5 * 8,     # byte 63 = 0x3F, high nibble 3
+        (4, 17): 49 * 1 - 0.5 * 2,    # byte 81 = 0x51, low nibble 1
+        (6, 31): 37 * 15 - 0.5 * 38,  # byte 127 = 0x7F, low nibble 15
+        (7, 0): 23 * 6 - 0.5 * 56,    # byte 96 = 0x60, high nibble 6
+    }
+    for (s, j), v in cases.items():
+        assert w[32 * s + j] == v, (s, j, w[32 * s + j], v)
+    nib, d, dmin, sc, mn = oracle.q4k_decode(_q4k_worked_block(), 1, 256)
+    assert d[0, 0] == 0x3C00 and dmin[0, 0] == 0x3800
+    assert [(int(a), int(b)) for a, b in zip(sc[0], mn[0])] == Q4K_SCALE_EXPECT
+    assert nib[0, 32 * 2 + 10] == (32 + 10) & 15 and nib[0, 32 * 5 + 3] == (64 + 3) >> 4
+
+
+def test_q4k_dot_equals_dequantized_matmul():
+    """The block-scaled form with the activation's ssum carrying the min term equals the plain f64
+    matmul of the dequantized weights and the dequantized activation (da * qa)."""
+    N, K, T = 5, 768, 3
+    blocks = synth.q4k_blocks(N, K, 950)
+    x = synth.normal((T, K), stream=951)
+    qa, da, ssum = oracle.quantize(x)
+    ref, norm = oracle.q4k_gemm(blocks, N, K, qa, da, ssum)
+    a = qa.astype(np.float64) * np.repeat(oracle.f16_to_f64(da), 32, axis=1)
+    direct = a @ oracle.q4k_dequant(blocks, N, K).T
+    assert np.all(np.abs(ref - direct) <= 1e-12 * norm)
+    # and one cell by pure-Python loops over the dequantized values
+    w = oracle.q4k_dequant(blocks, N, K)
+    s = 0.0
+    for k in range(K):
+        s += float(w[2, k]) * float(a[1, k])
+    assert abs(ref[1, 2] - s) <= 1e-12 * norm[1, 2]
+    pr, pn = oracle.q4k_dot_pairs(blocks, N, K, qa, da, ssum, np.array([1, 0]), np.array([2, 4]))
+    assert pr[0] == ref[1, 2] and pr[1] == ref[0, 4] and pn[0] == norm[1, 2]
+
+
+def test_q4k_degenerate_blocks():
+    """All-zero values leave only the min term -dmin*m*ssum; dmin = 0 leaves only d*sc*isum."""
+    K = 256
+    x = synth.normal((1, K), stream=952)
+    qa, da, ssum = oracle.quantize(x)
+    blk = _q4k_worked_block()
+    zero_vals = blk.copy()
+    zero_vals[16:] = 0
+    ref, _ = oracle.q4k_gemm(zero_vals, 1, K, qa, da, ssum)
+    expect = -sum(float(oracle.f16_to_f64(da[0, s])) * 0.5 * m * int(ssum[0, s])
+                  for s, (_, m) in enumerate(Q4K_SCALE_EXPECT))
+    assert ref[0, 0] == pytest.approx(expect, rel=1e-14, abs=0)
+    no_min = blk.copy()
+    no_min[2:4] = 0
+    ref2, _ = oracle.q4k_gemm(no_min, 1, K, qa, da, ssum)
+    w = oracle.q4k_dequant(no_min, 1, K)[0]
+    a = qa[0].astype(np.float64) * np.repeat(oracle.f16_to_f64(da[0]), 32)
+    assert ref2[0, 0] == pytest.approx(float(np.dot(w, a)), rel=1e-13)
