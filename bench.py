@@ -388,6 +388,33 @@ def bench_prefill_swiglu(D, reps):
     return out
 
 
+def bench_prefill_q4k(D, reps):
+    """q4_K gate and up projections over the rms-class plane (T=3325, d=3584, N=18944 each)."""
+    import synth
+    torch, q8 = D.torch, D.q8
+    T, K = 3325, 3584
+    x = D.tensor("prefill_rms", "x")
+    w = D.tensor("prefill_rms", "w_norm")
+    pq, ps = q8.alloc_act(T, K, q8.LAYOUT_PLANE64)
+    t = stats(time_each(D, lambda i: q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_PLANE64, None, pq, ps, f32=False),
+                        reps))
+    out = {"rmsnorm_quant_plane64_no_f32": {**t, "bytes": rms_bytes(T, K, 1) - T * K * 4}}
+    total_us = t["mean_us"]
+    for name in ("Wg", "Wu"):
+        blocks = D.upload(synth.q4k_tensor("prefill_q4k", name))
+        W = q8.Q4KWeights(blocks, K)
+        C = torch.empty((T, W.n), device=D.dev)
+        tg = stats(time_each(D, lambda i: q8.q4k_gemm(W, pq, ps, T, C), reps))
+        e = gemm_entry(tg, T, W.n, K)
+        e["min_bytes"] = T * K + (T // 64 + 1) * (K // 32) * 256 + blocks.numel() + T * W.n * 4
+        e["GBps_min_bytes"] = e["min_bytes"] / tg["mean_us"] / 1e3
+        out[f"q4k_gemm_{name}_{W.n}x{K}"] = e
+        total_us += tg["mean_us"]
+        del W, C, blocks
+    out["slice_tok_per_s"] = T / (total_us * 1e-6)
+    return out
+
+
 def bench_lm_head(D, reps):
     torch, q8 = D.torch, D.q8
     wl = "lm_head"
@@ -505,7 +532,8 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--reps", type=int, default=20, help="timed launches per kernel in the per-config section")
-    ap.add_argument("--configs", default="all", help="comma list of: decode,gemv2048,prefill_rms,prefill_swiglu,lm_head")
+    ap.add_argument("--configs", default="all",
+                    help="comma list of: decode,gemv2048,prefill_rms,prefill_swiglu,lm_head,prefill_q4k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall-clock budget of the oracle CPU baseline")
     args = ap.parse_args()
@@ -517,11 +545,13 @@ def main():
     D = Dev()
     torch = D.torch
     torch.cuda.set_device(0)
-    which = set(["decode", "gemv2048", "prefill_rms", "prefill_swiglu", "lm_head"]) if args.configs == "all" \
+    which = set(["decode", "gemv2048", "prefill_rms", "prefill_swiglu", "lm_head", "prefill_q4k"]) \
+        if args.configs == "all" \
         else set(args.configs.split(","))
     if "decode" not in which:  # profiling a subset: no headline line
         for name, fn in (("gemv2048", bench_gemv2048), ("prefill_rms", bench_prefill_rms),
-                         ("prefill_swiglu", bench_prefill_swiglu), ("lm_head", bench_lm_head)):
+                         ("prefill_swiglu", bench_prefill_swiglu), ("lm_head", bench_lm_head),
+                         ("prefill_q4k", bench_prefill_q4k)):
             if name in which:
                 log(f"[{name}] running")
                 print(json.dumps({name: fn(D, args.reps)}), flush=True)
@@ -533,7 +563,8 @@ def main():
     log(f"[decode] {dec['value_GBps']:.1f} GB/s, {dec['ms_per_step'] * 1e3:.2f} us/step")
     per = {}
     for name, fn in (("gemv2048", bench_gemv2048), ("prefill_rms", bench_prefill_rms),
-                     ("prefill_swiglu", bench_prefill_swiglu), ("lm_head", bench_lm_head)):
+                     ("prefill_swiglu", bench_prefill_swiglu), ("lm_head", bench_lm_head),
+                     ("prefill_q4k", bench_prefill_q4k)):
         if name in which:
             log(f"[{name}] running")
             per[name] = fn(D, args.reps)

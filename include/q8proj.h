@@ -76,6 +76,20 @@ typedef struct q8_weights {
     const uint16_t* d;  /* device, [N][K/32] f16 bits, 2-byte aligned */
 } q8_weights;
 
+/* q4_K weights ([P3] s2-s3.2): row-major [N][K/256] super-blocks of 144 bytes
+ * each -- f16 d at +0, f16 dmin at +2, 12 bytes of packed 6-bit sub-block
+ * scales and mins at +4, 128 bytes of 4-bit values at +16. Value j of the
+ * 32-value sub-block s is the low (s even) or high (s odd) nibble of byte
+ * 16 + 32*(s/2) + j; w = d*sc_s*nib - dmin*m_s. The 6-bit fields: for s < 4,
+ * sc = b[s] & 63 and m = b[s+4] & 63; for s >= 4, sc = (b[s+4] & 15) |
+ * (b[s-4] >> 6) << 4 and m = (b[s+4] >> 4) | (b[s] >> 6) << 4, with b the
+ * 12 scale bytes (the GGUF q4_K layout). */
+typedef struct q4k_weights {
+    int64_t n;              /* output rows N */
+    int64_t k;              /* reduction width K, a positive multiple of 256 */
+    const uint8_t* blocks;  /* device, [N][K/256] x 144 bytes, 16-byte aligned */
+} q4k_weights;
+
 /* ABI version (Q8PROJ_ABI_VERSION of the built library). */
 int q8_abi_version(void);
 
@@ -195,6 +209,20 @@ int q8_gemm(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64
  */
 int q8_gemm_shared_multi(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t,
                          float* const* c, const int64_t* ldc, void* stream);
+
+/*
+ * Prefill GEMM with q4_K weights over a PLANE64 q8_0 activation ([P3] s2:
+ * the weight side is staged as raw bytes and unpacked at matrix-op time):
+ *   C[t][n] = sum over 32-value sub-blocks b of
+ *             f16(da[t,b]) * (f16(d)*sc_b * isum[t,n,b] - f16(dmin)*m_b * ssum[t,b]),
+ *   isum = sum_j nib[n, 32b+j] * qa[t, 32b+j], ssum = the activation block's
+ *   stored sum of its q values ([P2] s2.1: kept for the min-term correction).
+ * a_qs, a_sd: a PLANE64 activation of T tokens and width W->k. C: [T][ldc]
+ * f32, ldc >= N; only columns n < N of rows t < T are written.
+ * K a multiple of 256 and <= 2^24 (Q8_ESHAPE otherwise).
+ */
+int q4k_gemm(const q4k_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t, float* c, int64_t ldc,
+             void* stream);
 
 /*
  * Load-time conversion of GGUF Q8_0 blocks (device, [N][K/32] x 34 bytes,

@@ -8,11 +8,13 @@ from . import q8lib  # noqa: F401
 from .q8lib import (  # noqa: F401
     LAYOUT_PLANE64,
     LAYOUT_ROW,
+    Q4KWeights,
     Q8Error,
     Q8Weights,
     act_bytes,
     alloc_act,
     gemv_plan,
+    q4k_gemm,
     q8_gemm,
     q8_gemm_shared_multi,
     q8_gemv,

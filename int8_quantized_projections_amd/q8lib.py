@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
             "q8_gemv_shared_multi_ex": ([ci, ctypes.POINTER(wp), vp, vp, ctypes.POINTER(vp), ci, vp], ci),
             "q8_gemv_plan": ([i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(i64)], ci),
             "q8_gemm": ([wp, vp, vp, i64, vp, i64, vp], ci),
+            "q4k_gemm": ([ctypes.POINTER(_Q4KWeights), vp, vp, i64, vp, i64, vp], ci),
             "q8_gemm_shared_multi": ([ci, ctypes.POINTER(wp), vp, vp, i64, ctypes.POINTER(vp), ctypes.POINTER(i64), vp],
                                      ci),
             "q8_weights_repack": ([vp, i64, i64, vp, vp, vp], ci),
@@ -133,6 +134,38 @@ class Q8Weights:
     def rows(self, start: int, stop: int) -> "Q8Weights":
         """A band of output rows (a pointer offset and a smaller N)."""
         return Q8Weights(self.qs[start:stop], self.d[start:stop])
+
+
+class _Q4KWeights(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("blocks", ctypes.c_void_p)]
+
+
+@dataclass
+class Q4KWeights:
+    """q4_K weights on the device: uint8 [N, K/256*144] (raw 144-byte super-blocks, row-major)."""
+    blocks: torch.Tensor
+    k: int
+
+    @property
+    def n(self) -> int:
+        return self.blocks.shape[0]
+
+    def struct(self) -> _Q4KWeights:
+        assert self.blocks.dtype == torch.uint8 and self.blocks.is_contiguous()
+        assert self.blocks.shape[1] == self.k // 256 * 144
+        return _Q4KWeights(self.n, self.k, _ptr(self.blocks))
+
+
+def q4k_gemm(W: Q4KWeights, a_qs: torch.Tensor, a_sd: torch.Tensor, t: int, C=None, ldc: int | None = None):
+    """C [t, N] = q4_K weights x PLANE64 q8_0 activation (see include/q8proj.h)."""
+    if C is None:
+        C = torch.empty((t, W.n), dtype=torch.float32, device=a_qs.device)
+    if ldc is None:
+        ldc = C.shape[-1] if C.dim() > 1 else W.n
+    ws = W.struct()
+    _check(lib().q4k_gemm(ctypes.byref(ws), _ptr(a_qs), _ptr(a_sd), t, _ptr(C), ldc, _stream(a_qs.device)),
+           "q4k_gemm")
+    return C
 
 
 def q8_weights_repack(blocks: torch.Tensor, n: int, k: int) -> Q8Weights:

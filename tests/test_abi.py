@@ -121,6 +121,18 @@ def test_gemv_and_gemm_reject_before_launch(L):
     assert L.q8_gemm(ctypes.byref(w), f, f + 1, 5, f, 8, None) == Q8_EALIGN
     assert L.q8_gemm(ctypes.byref(w), f, f, 0, f, 8, None) == Q8_OK  # T = 0: no-op
     assert L.q8_gemm(ctypes.byref(_w(8, (1 << 24) + 32)), f, f, 5, f, 8, None) == Q8_ESHAPE  # K > 2^24
+    # q4_K gemm: K a multiple of 256, blocks 16-byte aligned
+    q4 = lambda n, k, b=f: ctypes.byref(q8lib._Q4KWeights(n, k, b))
+    assert L.q4k_gemm(None, f, f, 5, f, 8, None) == Q8_EINVAL
+    assert L.q4k_gemm(q4(8, 288), f, f, 5, f, 8, None) == Q8_ESHAPE
+    assert L.q4k_gemm(q4(8, 512), f, f, 5, f, 4, None) == Q8_ESHAPE  # ldc < N
+    assert L.q4k_gemm(q4(8, 512), f, f, -1, f, 8, None) == Q8_ESHAPE
+    assert L.q4k_gemm(q4(8, 512, None), f, f, 5, f, 8, None) == Q8_EINVAL
+    assert L.q4k_gemm(q4(8, 512), None, f, 5, f, 8, None) == Q8_EINVAL
+    assert L.q4k_gemm(q4(8, 512, f + 8), f, f, 5, f, 8, None) == Q8_EALIGN
+    assert L.q4k_gemm(q4(8, 512), f, f + 2, 5, f, 8, None) == Q8_EALIGN
+    assert L.q4k_gemm(q4(8, 512), f, f, 0, f, 8, None) == Q8_OK  # T = 0: no-op
+    assert L.q4k_gemm(q4(0, 512), f, f, 5, f, 0, None) == Q8_OK  # N = 0: no-op
     # grouped gemm: m range, K must agree, every member's ldc and pointers checked
     def grouped(ws, cs, ldcs, t=5, aq=f, asd=f, m=None):
         wa = (ctypes.POINTER(q8lib._Weights) * len(ws))(*[ctypes.pointer(x) for x in ws])

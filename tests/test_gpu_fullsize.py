@@ -174,3 +174,27 @@ def test_lm_head_full():
     assert_norm(to_np(logits), ref, norm, 1e-5, "lm head gemv 152064x3584")
     pq, ps, qo, do, _ = plane_act(r512.astype(np.float32))
     check_gemm_cells(W, wq, wd, qo, do, pq, ps, 512, "lm head gemm T=512")
+
+
+def test_prefill_q4k_full():
+    """q4_K gate and up projections (N=18944, K=3584) over the T=3325 rms-class plane."""
+    x = synth.tensor("prefill_rms", "x")
+    w = synth.tensor("prefill_rms", "w_norm")
+    T, K = x.shape
+    y_ref = oracle.rmsnorm_f64(x, w, EPS)
+    pq, ps, qo, do, so = plane_act(y_ref.astype(np.float32))
+    del y_ref
+    for name in ("Wg", "Wu"):
+        blocks = synth.q4k_tensor("prefill_q4k", name)
+        N = blocks.shape[0]
+        W = q8lib.Q4KWeights(up(blocks), K)
+        C = poisoned(T * N, torch.float32, 0xFF).view(T, N)
+        q8lib.q4k_gemm(W, pq, ps, T, C)
+        torch.cuda.synchronize()
+        Cn = to_np(C)
+        assert not np.isnan(Cn).any(), f"q4k {name}: unwritten output cells"
+        pt, pn = sample_cells(T, N)
+        ref, norm = oracle.q4k_dot_pairs(blocks, N, K, qo, do, so, pt, pn)
+        assert_norm(Cn[pt, pn], ref, norm, 1e-5, f"q4k_gemm {name} {T}x{N}x{K}")
+        del W, C, Cn
+        torch.cuda.empty_cache()
