@@ -12,9 +12,12 @@
 //   sum_j w_j * da*qa_j = da * (d*sc_b * isum_b - dmin*m_b * ssum_b),
 //   isum_b = sum_j nib_j * qa_j  (exact: v_mfma_i32_32x32x32_i8 on the
 //   unpacked nibbles 0..15, which are valid signed int8 values).
-// The first term is the q8_gemm epilogue with dw replaced by d*sc_b; the min
-// term adds one DPP FMA per element and block: acc += (da*ssum)_t * (-dmin*m_b)_n,
-// with the per-token factor broadcast like the token scale.
+// The first term is the q8_gemm epilogue with dw replaced by d*sc_b. The min
+// term, sum_b c[t][b] * e[n][b] with c = da*ssum and e = -dmin*m, is itself a
+// small f32 matrix product (inner dimension K/32): per stage and 32x32 tile it
+// is two v_mfma_f32_32x32x2_f32 accumulating into the same registers as the
+// epilogue (all 32x32 MFMAs share one output layout), instead of one DPP FMA
+// per element and block on the vector ALU, which bounds this kernel.
 //
 // Staging: a stage is half a super-block (4 sub-blocks = 128 K) and reuses the
 // q8_gemm A side unchanged. The weight side copies, per row, the 16-byte
@@ -37,26 +40,16 @@ constexpr int kQ4Row = 80;     // LDS bytes per weight row per stage: header 16 
 constexpr int kQ4Pieces = 5;   // 16-byte pieces per row per stage
 static_assert(kKT == 4, "a stage is half a super-block");
 
-// acc[i] += c(lane 16q + R_i) * e: the min term, four registers at a time (the
-// same form as the scale FMA, with the per-lane factor e shared by all 16).
-#define Q4K_MIN_DPP4(a0, a1, a2, a3, cv, ev, R0, R1, R2, R3)                          \
-    asm volatile("v_fmac_f32_dpp %0, %4, %5 row_newbcast:" #R0 " row_mask:0xf bank_mask:0xf\n\t" \
-        "v_fmac_f32_dpp %1, %4, %5 row_newbcast:" #R1 " row_mask:0xf bank_mask:0xf\n\t" \
-        "v_fmac_f32_dpp %2, %4, %5 row_newbcast:" #R2 " row_mask:0xf bank_mask:0xf\n\t" \
-        "v_fmac_f32_dpp %3, %4, %5 row_newbcast:" #R3 " row_mask:0xf bank_mask:0xf"      \
-        : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)                                         \
-        : "v"(cv), "v"(ev))
-
-// One tile's block: the scale epilogue, then the min term. The first min
-// block starts with s_nop 1: c may be written by the VALU just before it.
-__device__ __forceinline__ void epilogue_q4k(float (&acc)[16], const v16f& d, float dsc, float nbias, float s,
-                                             float c, float e) {
-    epilogue(acc, d, dsc, nbias, s);
-    asm volatile("s_nop 1");
-    Q4K_MIN_DPP4(acc[0], acc[1], acc[2], acc[3], c, e, 0, 1, 2, 3);
-    Q4K_MIN_DPP4(acc[4], acc[5], acc[6], acc[7], c, e, 4, 5, 6, 7);
-    Q4K_MIN_DPP4(acc[8], acc[9], acc[10], acc[11], c, e, 8, 9, 10, 11);
-    Q4K_MIN_DPP4(acc[12], acc[13], acc[14], acc[15], c, e, 12, 13, 14, 15);
+// acc += A * B over one 32x32 tile: A[t][k] the token factors of two
+// sub-blocks, B[k][n] the row factors (lane l holds A[l%32][l/32] and
+// B[l/32][l%32]).
+__device__ __forceinline__ void min_mfma(float (&acc)[16], float a, float b) {
+    v16f x;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = acc[i];
+    x = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, x, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = x[i];
 }
 
 // 16 nibbles of a sub-block (low nibbles for even, high for odd sub-blocks) as
@@ -177,6 +170,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             dsc[kb] = dd * (float)sc;   // exact: 11 + 6 bits
             em[kb] = -(dm * (float)m);  // exact
         }
+        // min-term operands: e of sub-blocks khalf and 2+khalf of this lane's
+        // row; c of token 32h + lane%32 in the same sub-blocks
+        float eb[2], ca[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            eb[j] = khalf ? em[2 * j + 1] : em[2 * j];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t w = ls[(2 * j + khalf) * kGroup + 32 * h + (lane & 31)];
+                ca[h][j] = f16_value(w) * (float)(int16_t)(w >> 16);  // exact: 11 + 12 bits
+            }
+        }
         v4i raw[2];  // value bytes of sub-block pairs (0,1) and (2,3), this lane's half
 #pragma unroll
         for (int p = 0; p < 2; ++p) raw[p] = *reinterpret_cast<const v4i*>(lb + 16 + 32 * p + 16 * khalf);
@@ -201,19 +206,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 afrags(kb + 1, an, sn);
                 bn = bfrag(kb + 1);
             }
-            // token factors of this block: the scale da and da * ssum
-            float s[2], c[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                s[h] = f16_value(sw[h]);
-                c[h] = s[h] * (float)(int16_t)(sw[h] >> 16);
-            }
+            const float s0 = f16_value(sw[0]), s1 = f16_value(sw[1]);
             const v16i d0 = d;
             d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[1], bf, bias, 0, 0, 0);
-            epilogue_q4k(acc[0], __builtin_bit_cast(v16f, d0), dw, nbias, s[0], c[0], em[kb]);
+            epilogue(acc[0], __builtin_bit_cast(v16f, d0), dw, nbias, s0);
+            if (kb + 1 == kKT) {
+                min_mfma(acc[0], ca[0][0], eb[0]);
+                min_mfma(acc[0], ca[0][1], eb[1]);
+            }
             const v16i d1 = d;
             if (kb + 1 < kKT) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(an[0], bn, bias, 0, 0, 0);
-            epilogue_q4k(acc[1], __builtin_bit_cast(v16f, d1), dw, nbias, s[1], c[1], em[kb]);
+            epilogue(acc[1], __builtin_bit_cast(v16f, d1), dw, nbias, s1);
+            if (kb + 1 == kKT) {
+                min_mfma(acc[1], ca[1][0], eb[0]);
+                min_mfma(acc[1], ca[1][1], eb[1]);
+            }
             af[0] = an[0];
             af[1] = an[1];
             bf = bn;
