@@ -8,8 +8,10 @@ Thin numpy wrappers over ``q8_oracle.c`` (plain C, see its header for the
 page citations). Every function here computes what the pages define, in f64
 for floating point except the quantize, which the pages fix in f32.
 
-Parity pins live in ``tests/test_oracle_pins.py``. Nothing here is
-"parity unpinned".
+Parity pins live in ``tests/test_oracle_pins.py``. One reading is pinned
+only in part: the bit layout of q4_K's 6-bit scales and mins (the pages name
+the decode but not its layout; the GGUF layout is taken, and the pins fix it
+up to a permutation of bits), so that assignment is "parity unpinned".
 """
 from __future__ import annotations
 

@@ -322,11 +322,14 @@ void q8o_block_isums(const int8_t* wq, int64_t N, int64_t K, const int8_t* aq, i
  * 12 bytes of packed 6-bit sub-block scales and mins at +4, 128 bytes of
  * 4-bit values at +16. Sub-block s (values 32s..32s+31, s = 0..7) takes value
  * j from byte 16 + 32*(s/2) + j: its low nibble for even s, its high nibble
- * for odd s ([P3] s3.2, the listing's unpack). The value is
+ * for odd s ([P3] s3.2, the unpack of the staging branch). The value is
  *   w = d * sc_s * nib - dmin * m_s          (nib unsigned, 0..15)
- * ([P3] s3.2: "value = d*s*nib - dmin*m").
- * The pages call the 6-bit decode get_scale_min_k4 without its bit layout;
- * the GGUF q4_K layout is taken: with b the 12 bytes,
+ * ([P3] s3.2: the scale times the unsigned nibble, minus dmin times the min).
+ * The pages name the 6-bit decode (get_scale_min_k4) without giving its bit
+ * layout; the GGUF q4_K layout is taken. Its pins (a worked example, and that
+ * the 96 bits map one to one onto the sixteen 6-bit fields) fix it only up to
+ * a permutation of bits: which bit goes where is that format's, unpinned by
+ * the pages. With b the 12 bytes,
  *   s < 4 : sc = b[s] & 63,                     m = b[s+4] & 63
  *   s >= 4: sc = (b[s+4] & 15) | (b[s-4] >> 6) << 4,
  *           m  = (b[s+4] >> 4) | (b[s]   >> 6) << 4.
