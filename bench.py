@@ -241,9 +241,12 @@ def bench_decode(D, steps, warmup, log_reps):
         step(0)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    # the library's launch counters over the capture: launches per step, counted
+    q8.launch_counts_reset()
     with torch.cuda.graph(g):
         for i in range(steps):
             step(i)
+    counted = {k: v / steps for k, v in q8.launch_counts().items() if v}
     g.replay()  # untimed: graph upload / first replay
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -275,7 +278,8 @@ def bench_decode(D, steps, warmup, log_reps):
                                     "launches_per_step": 0}
     del g
     return {"ms_per_step": ms / steps, "step_bytes": step_bytes, "value_GBps": step_bytes * steps / (ms * 1e-3) / 1e9,
-            "copies": ncopy, "components": comp, "launches_per_step": len(parts)}
+            "copies": ncopy, "components": comp, "launches_per_step": sum(counted.values()),
+            "launch_counts_per_step": counted}
 
 
 # ---------------------------------------------------------------------------
@@ -589,7 +593,8 @@ def main():
         "config": {"workload": "decode_h7168", "batch": 1, "hidden": 7168,
                    "gemvs": "rmsnorm_quant ROW -> one grouped q8_gemv_shared_multi over N=4096/512/512/4096/"
                             "12288/96 (K=7168); q8_gemv_f32 N=4096 K=128 (its activation quantized in the launch)",
-                   "launches_per_step": dec["launches_per_step"], "weight_copies": dec["copies"],
+                   "launches_per_step": dec["launches_per_step"],
+                   "launch_counts_per_step": dec["launch_counts_per_step"], "weight_copies": dec["copies"],
                    "timing": "HIP graph of all timed steps, HIP events around the replay"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define Q8PROJ_ABI_VERSION 1
+#define Q8PROJ_ABI_VERSION 2
 
 /* return codes */
 #define Q8_OK 0
@@ -95,6 +95,42 @@ int q8_abi_version(void);
 
 /* Human-readable text of a return code (static storage). */
 const char* q8_strerror(int code);
+
+/*
+ * Launch counters ([P1] s3: a tiny kernel's cost is set by how often it is
+ * launched, not by its bytes; [P1] s5: count launches, and check the count
+ * against the model's structure -- layers, consumers -- rather than trusting
+ * a speedup). The library keeps one counter per entry point. Each counts the
+ * kernel launches that entry point has enqueued since the library was loaded
+ * or last reset: one per call that launched successfully. A call that returns
+ * an error, or has nothing to do (zero rows), adds nothing. Launches recorded
+ * into a HIP graph under stream capture count once, at capture; graph replays
+ * do not pass through the library and are not counted. Counting is atomic,
+ * process-wide and covers all devices.
+ */
+#define Q8_LAUNCH_QUANTIZE 0              /* q8_quantize */
+#define Q8_LAUNCH_RMSNORM_QUANT 1         /* rmsnorm_quant */
+#define Q8_LAUNCH_SWIGLU_QUANT 2          /* swiglu_quant */
+#define Q8_LAUNCH_GEMV 3                  /* q8_gemv */
+#define Q8_LAUNCH_GEMV_SHARED_MULTI 4     /* q8_gemv_shared_multi and q8_gemv_shared_multi_ex */
+#define Q8_LAUNCH_GEMV_F32 5              /* q8_gemv_f32 */
+#define Q8_LAUNCH_GEMM 6                  /* q8_gemm */
+#define Q8_LAUNCH_GEMM_SHARED_MULTI 7     /* q8_gemm_shared_multi */
+#define Q8_LAUNCH_Q4K_GEMM 8              /* q4k_gemm */
+#define Q8_LAUNCH_WEIGHTS_REPACK 9        /* q8_weights_repack */
+#define Q8_LAUNCH_COUNTERS 10
+
+/* Copies the first min(n, Q8_LAUNCH_COUNTERS) counters, in the order of the
+ * Q8_LAUNCH_* ids, into the host array counts. Returns Q8_LAUNCH_COUNTERS,
+ * or Q8_EINVAL (nothing copied) when n < 0 or counts is NULL with n > 0. */
+int q8_launch_counts(int64_t* counts, int n);
+
+/* Sets every launch counter to zero. */
+void q8_launch_counts_reset(void);
+
+/* Name of the entry point counter `id` counts (static storage), or NULL when
+ * id is not a Q8_LAUNCH_* id. */
+const char* q8_launch_counter_name(int id);
 
 /*
  * Bytes of the activation buffers for `rows` rows of width K in `layout`

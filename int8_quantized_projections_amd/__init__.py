@@ -14,6 +14,8 @@ from .q8lib import (  # noqa: F401
     act_bytes,
     alloc_act,
     gemv_plan,
+    launch_counts,
+    launch_counts_reset,
     q4k_gemm,
     q8_gemm,
     q8_gemm_shared_multi,

@@ -343,7 +343,7 @@ int check_member(const q8_weights* W, int64_t ldc, const float* c) {
     return Q8_OK;
 }
 
-int launch_gemm(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t,
+int launch_gemm(int counter, int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t,
                 float* const* c, const int64_t* ldc, hipStream_t stream) {
     if (m < 1 || m > kMaxMembers || W == nullptr || c == nullptr || ldc == nullptr) return Q8_EINVAL;
     if (t < 0) return Q8_ESHAPE;
@@ -391,17 +391,17 @@ int launch_gemm(int m, const q8_weights* const* W, const int8_t* a_qs, const uin
     else
         hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)tiles), dim3(256), 0, stream, a_qs, a_sd, M, t,
                            (int)W[0]->k, nb, (int)n_tiles, tiles);
-    return q8h::launch_status();
+    return q8h::launch_status(counter);
 }
 
 }  // namespace
 
 extern "C" int q8_gemm(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t, float* c,
                        int64_t ldc, void* stream) {
-    return launch_gemm(1, &W, a_qs, a_sd, t, &c, &ldc, (hipStream_t)stream);
+    return launch_gemm(Q8_LAUNCH_GEMM, 1, &W, a_qs, a_sd, t, &c, &ldc, (hipStream_t)stream);
 }
 
 extern "C" int q8_gemm_shared_multi(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
                                     int64_t t, float* const* c, const int64_t* ldc, void* stream) {
-    return launch_gemm(m, W, a_qs, a_sd, t, c, ldc, (hipStream_t)stream);
+    return launch_gemm(Q8_LAUNCH_GEMM_SHARED_MULTI, m, W, a_qs, a_sd, t, c, ldc, (hipStream_t)stream);
 }

@@ -276,5 +276,5 @@ extern "C" int q4k_gemm(const q4k_weights* W, const int8_t* a_qs, const uint32_t
     if (tiles > INT32_MAX) return Q8_ESHAPE;
     hipLaunchKernelGGL(k_gemm_q4k, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, a_qs, a_sd, W->blocks,
                        c, t, W->n, (int)W->k, nb, ldc, (int)n_tiles, tiles);
-    return q8h::launch_status();
+    return q8h::launch_status(Q8_LAUNCH_Q4K_GEMM);
 }

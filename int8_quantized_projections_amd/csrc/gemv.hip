@@ -297,8 +297,10 @@ int q8_gemv_plan(int64_t total_rows, int64_t k, int rows_per_wave, int* lanes_pe
     return Q8_OK;
 }
 
-int q8_gemv_shared_multi_ex(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
-                            float* const* y, int rows_per_wave, void* stream) {
+// The grouped GEMV behind q8_gemv, q8_gemv_shared_multi and _ex; `counter`
+// names the entry point whose launch counter a launch adds to.
+static int gemv_multi(int counter, int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
+                      float* const* y, int rows_per_wave, void* stream) {
     if (m < 1 || m > kMaxMats || W == nullptr || y == nullptr) return Q8_EINVAL;
     if (rows_per_wave != 0 && rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4) return Q8_EINVAL;
     GemvArgs a;
@@ -349,7 +351,12 @@ int q8_gemv_shared_multi_ex(int m, const q8_weights* const* W, const int8_t* a_q
         a.y[0] = a.y[first];
     }
     launch(p, nonempty > 1, (hipStream_t)stream, a, a_qs, a_sd, (int)K, nb);
-    return q8h::launch_status();
+    return q8h::launch_status(counter);
+}
+
+int q8_gemv_shared_multi_ex(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
+                            float* const* y, int rows_per_wave, void* stream) {
+    return gemv_multi(Q8_LAUNCH_GEMV_SHARED_MULTI, m, W, a_qs, a_sd, y, rows_per_wave, stream);
 }
 
 int q8_gemv_shared_multi(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
@@ -377,14 +384,14 @@ int q8_gemv_f32(const q8_weights* W, const float* x, float* y, void* stream) {
     const int nb = (int)(W->k / kQK);
     const Plan p = make_plan(W->n, nb, 0);
     launch_m<false, true>(p, (hipStream_t)stream, a, nullptr, nullptr, x, (int)W->k, nb);
-    return q8h::launch_status();
+    return q8h::launch_status(Q8_LAUNCH_GEMV_F32);
 }
 
 int q8_gemv(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, float* y, void* stream) {
     if (W == nullptr) return Q8_EINVAL;
     const q8_weights* ws[1] = {W};
     float* ys[1] = {y};
-    return q8_gemv_shared_multi_ex(1, ws, a_qs, a_sd, ys, 0, stream);
+    return gemv_multi(Q8_LAUNCH_GEMV, 1, ws, a_qs, a_sd, ys, 0, stream);
 }
 
 }  // extern "C"

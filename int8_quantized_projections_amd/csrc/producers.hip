@@ -331,7 +331,7 @@ int launch_elementwise(const float* a, const float* b, float* y, int64_t rows, i
         hipLaunchKernelGGL((k_elementwise<kDstPlane, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, upr,
                            units, qs, sd);
     }
-    return q8h::launch_status();
+    return q8h::launch_status(SWIGLU ? Q8_LAUNCH_SWIGLU_QUANT : Q8_LAUNCH_QUANTIZE);
 }
 
 template <int D, int WPR, int WAVES = kWavesPerWg>
@@ -409,6 +409,23 @@ extern "C" {
 
 int q8_abi_version(void) { return Q8PROJ_ABI_VERSION; }
 
+int q8_launch_counts(int64_t* counts, int n) {
+    if (n < 0 || (counts == nullptr && n > 0)) return Q8_EINVAL;
+    for (int i = 0; i < n && i < Q8_LAUNCH_COUNTERS; ++i) counts[i] = q8h::launches[i].load(std::memory_order_relaxed);
+    return Q8_LAUNCH_COUNTERS;
+}
+
+void q8_launch_counts_reset(void) {
+    for (int i = 0; i < Q8_LAUNCH_COUNTERS; ++i) q8h::launches[i].store(0, std::memory_order_relaxed);
+}
+
+const char* q8_launch_counter_name(int id) {
+    static const char* const names[Q8_LAUNCH_COUNTERS] = {
+        "q8_quantize", "rmsnorm_quant", "swiglu_quant", "q8_gemv", "q8_gemv_shared_multi",
+        "q8_gemv_f32", "q8_gemm", "q8_gemm_shared_multi", "q4k_gemm", "q8_weights_repack"};
+    return (id >= 0 && id < Q8_LAUNCH_COUNTERS) ? names[id] : nullptr;
+}
+
 const char* q8_strerror(int code) {
     switch (code) {
         case Q8_OK: return "ok";
@@ -470,7 +487,7 @@ int rmsnorm_quant(const float* x, const float* w, float eps, float* y, int64_t r
         dispatch_rms<kDstRow>(s, x, w, eps, y, rows, tpad, (int)k, nb, qs, sd);
     else
         dispatch_rms<kDstPlane>(s, x, w, eps, y, rows, tpad, (int)k, nb, qs, sd);
-    return q8h::launch_status();
+    return q8h::launch_status(Q8_LAUNCH_RMSNORM_QUANT);
 }
 
 int q8_weights_repack(const void* gguf_blocks, int64_t n, int64_t k, int8_t* qs, uint16_t* d, void* stream) {
@@ -482,7 +499,7 @@ int q8_weights_repack(const void* gguf_blocks, int64_t n, int64_t k, int8_t* qs,
     if (nblocks == 0) return Q8_OK;
     hipLaunchKernelGGL(k_repack, dim3((unsigned)q8h::ceil_div(nblocks, 256)), dim3(256), 0, (hipStream_t)stream,
                        reinterpret_cast<const uint16_t*>(gguf_blocks), nblocks, qs, d);
-    return q8h::launch_status();
+    return q8h::launch_status(Q8_LAUNCH_WEIGHTS_REPACK);
 }
 
 }  // extern "C"

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "q8proj.h"
 
 namespace q8 {
@@ -190,9 +192,16 @@ namespace q8h {
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-inline int launch_status() {
+// Launch counters of the entry points (Q8_LAUNCH_* ids), process-wide.
+inline std::atomic<int64_t> launches[Q8_LAUNCH_COUNTERS];
+
+// Status of the launch just made by the calling thread; a successful launch
+// adds one to the entry point's counter.
+inline int launch_status(int counter) {
     hipError_t e = hipGetLastError();
-    return e == hipSuccess ? Q8_OK : Q8_ELAUNCH;
+    if (e != hipSuccess) return Q8_ELAUNCH;
+    launches[counter].fetch_add(1, std::memory_order_relaxed);
+    return Q8_OK;
 }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

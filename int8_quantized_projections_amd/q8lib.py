@@ -63,6 +63,9 @@ def lib() -> ctypes.CDLL:
             "q8_gemm_shared_multi": ([ci, ctypes.POINTER(wp), vp, vp, i64, ctypes.POINTER(vp), ctypes.POINTER(i64), vp],
                                      ci),
             "q8_weights_repack": ([vp, i64, i64, vp, vp, vp], ci),
+            "q8_launch_counts": ([ctypes.POINTER(i64), ci], ci),
+            "q8_launch_counts_reset": ([], None),
+            "q8_launch_counter_name": ([ci], ctypes.c_char_p),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -101,6 +104,24 @@ def _ptr(t: torch.Tensor | None) -> int | None:
 # ---------------------------------------------------------------------------
 # Buffers
 # ---------------------------------------------------------------------------
+def launch_counts() -> dict[str, int]:
+    """The library's launch counter of every entry point, by entry-point name (see
+    q8_launch_counts in include/q8proj.h)."""
+    L = lib()
+    n = L.q8_launch_counts(None, 0)  # the number of counters
+    if n < 0:
+        raise Q8Error(n, "q8_launch_counts")
+    buf = (ctypes.c_int64 * n)()
+    rc = L.q8_launch_counts(buf, n)
+    if rc != n:
+        raise Q8Error(rc, "q8_launch_counts")
+    return {L.q8_launch_counter_name(i).decode(): int(buf[i]) for i in range(n)}
+
+
+def launch_counts_reset() -> None:
+    lib().q8_launch_counts_reset()
+
+
 def act_bytes(rows: int, k: int, layout: int) -> tuple[int, int]:
     q = ctypes.c_size_t()
     s = ctypes.c_size_t()

@@ -41,7 +41,7 @@ def test_exports_every_declared_function(L):
     assert len(names) >= 12
     for n in names:
         assert hasattr(L, n), f"{n} declared in q8proj.h but not exported"
-    assert L.q8_abi_version() == 1
+    assert L.q8_abi_version() == 2
     assert L.q8_strerror(-3).decode().startswith("pointer not aligned")
 
 
@@ -176,3 +176,49 @@ def test_gemv_rows_per_wave_threshold(L):
     # the grid never exceeds the persistent cap, and covers small N fully
     assert q8lib.gemv_plan(152064, 3584)["workgroups"] == 4096 // 4
     assert q8lib.gemv_plan(96, 7168)["workgroups"] == 24
+
+
+def declared_launch_counters():
+    """{id: entry point} from the Q8_LAUNCH_* defines of the header (the first name in each comment)."""
+    text = open(HEADER).read()
+    ids = {int(i): name for i, name in re.findall(r"#define Q8_LAUNCH_\w+ (\d+)[ \t]+/\* (\w+)", text)}
+    total = int(re.search(r"#define Q8_LAUNCH_COUNTERS (\d+)", text).group(1))
+    return ids, total
+
+
+def test_launch_counter_api(L):
+    ids, total = declared_launch_counters()
+    assert sorted(ids) == list(range(total)) and total >= 10
+    assert L.q8_launch_counts(None, 0) == total
+    for i, name in ids.items():
+        assert L.q8_launch_counter_name(i).decode() == name
+    assert L.q8_launch_counter_name(-1) is None and L.q8_launch_counter_name(total) is None
+    buf = (ctypes.c_int64 * (total + 2))(*([-7] * (total + 2)))
+    assert L.q8_launch_counts(None, 3) == Q8_EINVAL
+    assert L.q8_launch_counts(buf, -1) == Q8_EINVAL
+    assert list(buf) == [-7] * (total + 2)
+    L.q8_launch_counts_reset()
+    assert L.q8_launch_counts(buf, 3) == total  # copies only the first 3
+    assert list(buf) == [0, 0, 0] + [-7] * (total - 1)
+    assert L.q8_launch_counts(buf, total + 2) == total  # never past the last counter
+    assert list(buf) == [0] * total + [-7, -7]
+    assert q8lib.launch_counts() == {name: 0 for name in ids.values()}
+
+
+def test_rejected_and_empty_calls_launch_nothing(L):
+    """A call that fails validation, or has nothing to do, adds to no counter."""
+    L.q8_launch_counts_reset()
+    test_quantize_and_producers_reject_before_launch(L)
+    test_gemv_and_gemm_reject_before_launch(L)
+    f = FAKE
+    # zero rows / tokens / outputs: valid calls with nothing to launch
+    assert L.q8_quantize(f, 0, 64, 0, f, f, None) == Q8_OK
+    assert L.q8_quantize(f, 0, 64, 1, f, f, None) == Q8_OK
+    assert L.swiglu_quant(f, f, f, 0, 64, 1, f, f, None) == Q8_OK
+    assert L.rmsnorm_quant(f, f, 1e-6, f, 0, 64, 0, f, f, None) == Q8_OK
+    W = q8lib._Weights(0, 64, ctypes.c_void_p(f), ctypes.c_void_p(f))
+    assert L.q8_gemv(ctypes.byref(W), f, f, f, None) == Q8_OK
+    W1 = q8lib._Weights(8, 64, ctypes.c_void_p(f), ctypes.c_void_p(f))
+    assert L.q8_gemm(ctypes.byref(W1), f, f, 0, f, 8, None) == Q8_OK
+    assert L.q8_weights_repack(f, 0, 64, f, f, None) == Q8_OK
+    assert all(v == 0 for v in q8lib.launch_counts().values())
