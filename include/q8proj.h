@@ -118,7 +118,8 @@ const char* q8_strerror(int code);
 #define Q8_LAUNCH_GEMM_SHARED_MULTI 7     /* q8_gemm_shared_multi */
 #define Q8_LAUNCH_Q4K_GEMM 8              /* q4k_gemm */
 #define Q8_LAUNCH_WEIGHTS_REPACK 9        /* q8_weights_repack */
-#define Q8_LAUNCH_COUNTERS 10
+#define Q8_LAUNCH_GEMV_SHARED_MULTI_PLUS_F32 10  /* q8_gemv_shared_multi_plus_f32 (1 launch, or 2: see there) */
+#define Q8_LAUNCH_COUNTERS 11
 
 /* Copies the first min(n, Q8_LAUNCH_COUNTERS) counters, in the order of the
  * Q8_LAUNCH_* ids, into the host array counts. Returns Q8_LAUNCH_COUNTERS,
@@ -214,6 +215,23 @@ int q8_gemv_shared_multi(int m, const q8_weights* const* W, const int8_t* a_qs, 
  */
 int q8_gemv_shared_multi_ex(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
                             float* const* y, int rows_per_wave, void* stream);
+
+/*
+ * q8_gemv_shared_multi(m, W, a_qs, a_sd, y) and q8_gemv_f32(Wx, x, yx) in one
+ * launch ([P1] s6: the decode projections of a layer read a few activations at
+ * different N; [P1] s3: at decode every launch costs microseconds while its
+ * bytes cost less). The two GEMVs are independent: the grouped one reads the
+ * ROW-layout q8_0 activation (a_qs, a_sd) and writes y[i]; the other reads the
+ * f32 activation x of width Wx->k <= 8192, quantized inside the launch, and
+ * writes yx. Arguments, layouts and errors are those of the two calls, and both
+ * are validated before anything is launched. The outputs are bit-identical to
+ * the two separate calls. One launch serves the grouped part at K in
+ * (2048, 8192] together with the f32 part at Wx->k in (64, 512] (the rows per
+ * wave that q8_gemv_plan picks for each part must be at most 2, and 1 for the
+ * f32 part). Other shapes, or an empty part, make the two launches back to back.
+ */
+int q8_gemv_shared_multi_plus_f32(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
+                                  float* const* y, const q8_weights* Wx, const float* x, float* yx, void* stream);
 
 /*
  * The GEMV launch plan for `total_rows` rows of width K (host only):

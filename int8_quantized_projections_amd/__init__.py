@@ -22,6 +22,7 @@ from .q8lib import (  # noqa: F401
     q8_gemv,
     q8_gemv_f32,
     q8_gemv_shared_multi,
+    q8_gemv_shared_multi_plus_f32,
     q8_quantize,
     q8_weights_repack,
     rmsnorm_quant,

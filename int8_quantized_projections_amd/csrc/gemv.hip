@@ -74,15 +74,15 @@ __device__ __forceinline__ int dot32(const uint4& w0, const uint4& w1, const uin
 // are the concatenation of several matrices (the grouped launch); the
 // per-row arithmetic is the same code either way. F32A: the activation is
 // f32 (ax) and each lane quantizes the blocks it holds (one chunk only).
-template <int W, int NBL, int R, bool MULTI, bool F32A = false>
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __restrict__ aq,
-                                              const uint32_t* __restrict__ asd, const float* __restrict__ ax, int K,
-                                              int nb, int64_t groups) {
+// The GEMV of one wave: wave `wave_id` of `nwaves` takes row groups wave_id,
+// wave_id + nwaves, ...
+template <int W, int NBL, int R, bool MULTI, bool F32A>
+__device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __restrict__ aq,
+                                         const uint32_t* __restrict__ asd, const float* __restrict__ ax, int K,
+                                         int nb, int64_t groups, int64_t wave_id, int64_t nwaves) {
     constexpr int G = kWave / W;  // row slots per wave
     constexpr int CH = W * NBL;   // blocks per chunk
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerWg + (threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerWg;
     const int slot = lane / W, u = lane % W;
     const int nchunks = (nb + CH - 1) / CH;
 
@@ -200,6 +200,34 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __res
     for (int64_t gi = wave_id + nwaves; gi < groups; gi += nwaves) body(gi, std::false_type{});
 }
 
+template <int W, int NBL, int R, bool MULTI, bool F32A = false>
+__global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __restrict__ aq,
+                                              const uint32_t* __restrict__ asd, const float* __restrict__ ax, int K,
+                                              int nb, int64_t groups) {
+    gemv_run<W, NBL, R, MULTI, F32A>(args, aq, asd, ax, K, nb, groups,
+                                     (int64_t)blockIdx.x * kWavesPerWg + (threadIdx.x >> 6),
+                                     (int64_t)gridDim.x * kWavesPerWg);
+}
+
+// Two independent GEMVs in one launch: workgroups [0, wgs2) run the f32-activation
+// GEMV (a2, its activation x2 quantized in the launch, W2 lanes per row), the rest
+// the grouped GEMV over the q8_0 activation (a1). Each part runs exactly the
+// code of its own kernel, so the outputs are those of the two launches.
+template <int W, int NBL, int R, int W2>
+__global__ __launch_bounds__(256) void k_gemv_pair(GemvArgs a1, const int8_t* __restrict__ aq,
+                                                   const uint32_t* __restrict__ asd, int K1, int nb1,
+                                                   int64_t groups1, GemvArgs a2, const float* __restrict__ x2,
+                                                   int K2, int nb2, int64_t groups2, int wgs2) {
+    const int w = threadIdx.x >> 6;
+    if ((int)blockIdx.x < wgs2)
+        gemv_run<W2, 1, 1, false, true>(a2, nullptr, nullptr, x2, K2, nb2, groups2,
+                                        (int64_t)blockIdx.x * kWavesPerWg + w, (int64_t)wgs2 * kWavesPerWg);
+    else
+        gemv_run<W, NBL, R, true, false>(a1, aq, asd, nullptr, K1, nb1, groups1,
+                                         (int64_t)(blockIdx.x - wgs2) * kWavesPerWg + w,
+                                         (int64_t)(gridDim.x - wgs2) * kWavesPerWg);
+}
+
 struct Plan {
     int lanes;         // W
     int nbl;           // blocks per lane per chunk
@@ -284,26 +312,23 @@ int check_weights(const q8_weights* w) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int q8_gemv_plan(int64_t total_rows, int64_t k, int rows_per_wave, int* lanes_per_row, int* rows_per_wave_out,
-                 int64_t* workgroups) {
-    if (total_rows < 0 || k <= 0 || (k % kQK) != 0) return Q8_ESHAPE;
-    if (rows_per_wave != 0 && rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4) return Q8_EINVAL;
-    const Plan p = make_plan(total_rows, (int)(k / kQK), rows_per_wave);
-    if (lanes_per_row) *lanes_per_row = p.lanes;
-    if (rows_per_wave_out) *rows_per_wave_out = p.rows;
-    if (workgroups) *workgroups = total_rows == 0 ? 0 : p.workgroups;
-    return Q8_OK;
-}
+// A validated GEMV launch: its arguments and plan; `empty` when there is
+// nothing to compute.
+struct GemvJob {
+    GemvArgs a;
+    Plan p;
+    int K = 0, nb = 0;
+    bool multi = false, empty = true;
+};
 
-// The grouped GEMV behind q8_gemv, q8_gemv_shared_multi and _ex; `counter`
-// names the entry point whose launch counter a launch adds to.
-static int gemv_multi(int counter, int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
-                      float* const* y, int rows_per_wave, void* stream) {
+// Validation and launch arguments of the grouped GEMV (q8_gemv, q8_gemv_shared_multi).
+int prepare_multi(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
+                         float* const* y, int rows_per_wave, GemvJob& j) {
     if (m < 1 || m > kMaxMats || W == nullptr || y == nullptr) return Q8_EINVAL;
     if (rows_per_wave != 0 && rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4) return Q8_EINVAL;
-    GemvArgs a;
+    GemvArgs& a = j.a;
     int64_t total = 0;
     const int64_t K = W[0] ? W[0]->k : 0;
     for (int i = 0; i < m; ++i) {
@@ -335,9 +360,11 @@ static int gemv_multi(int counter, int m, const q8_weights* const* W, const int8
     }
     if (a_qs == nullptr || a_sd == nullptr) return Q8_EINVAL;
     if (!q8h::aligned(a_qs, 16) || !q8h::aligned(a_sd, 4)) return Q8_EALIGN;
-    if (total == 0) return Q8_OK;
-    const int nb = (int)(K / kQK);
-    const Plan p = make_plan(total, nb, rows_per_wave);
+    j.empty = total == 0;
+    if (j.empty) return Q8_OK;
+    j.K = (int)K;
+    j.nb = (int)(K / kQK);
+    j.p = make_plan(total, j.nb, rows_per_wave);
     // one non-empty member: the plain kernel, reading member 0's pointers
     int nonempty = 0, first = 0;
     for (int i = m - 1; i >= 0; --i)
@@ -345,12 +372,114 @@ static int gemv_multi(int counter, int m, const q8_weights* const* W, const int8
             ++nonempty;
             first = i;
         }
-    if (nonempty == 1) {
+    j.multi = nonempty > 1;
+    if (!j.multi) {
         a.wq[0] = a.wq[first];
         a.wd[0] = a.wd[first];
         a.y[0] = a.y[first];
     }
-    launch(p, nonempty > 1, (hipStream_t)stream, a, a_qs, a_sd, (int)K, nb);
+    return Q8_OK;
+}
+
+// Validation and launch arguments of the f32-activation GEMV (q8_gemv_f32).
+int prepare_f32(const q8_weights* W, const float* x, float* y, GemvJob& j) {
+    int rc = check_weights(W);
+    if (rc) return rc;
+    if (W->k > kMaxF32K) return Q8_ESHAPE;
+    if (x == nullptr || (y == nullptr && W->n > 0)) return Q8_EINVAL;
+    if (!q8h::aligned(x, 16) || !q8h::aligned(y, 4)) return Q8_EALIGN;
+    j.empty = W->n == 0;
+    if (j.empty) return Q8_OK;
+    GemvArgs& a = j.a;
+    for (int i = 0; i < kMaxMats; ++i) {
+        a.wq[i] = W->qs;
+        a.wd[i] = W->d;
+        a.y[i] = y;
+        a.off[i] = i == 0 ? 0 : INT64_MAX;
+    }
+    a.total = W->n;
+    a.safe_q = W->qs;
+    a.safe_d = W->d;
+    j.K = (int)W->k;
+    j.nb = (int)(W->k / kQK);
+    j.p = make_plan(W->n, j.nb, 0);
+    return Q8_OK;
+}
+
+void launch_multi(const GemvJob& j, hipStream_t s, const int8_t* a_qs, const uint32_t* a_sd) {
+    launch(j.p, j.multi, s, j.a, a_qs, a_sd, j.K, j.nb);
+}
+
+void launch_f32(const GemvJob& j, hipStream_t s, const float* x) {
+    launch_m<false, true>(j.p, s, j.a, nullptr, nullptr, x, j.K, j.nb);
+}
+
+// The pair kernel is instantiated for the grouped part with 64 lanes per row,
+// 2 or 4 blocks per lane (K in (2048, 8192]) and 1 or 2 rows per wave, and the
+// f32 part with 4, 8 or 16 lanes per row and one block per lane (K in (64, 512]).
+bool pair_supported(const Plan& p1, const Plan& p2) {
+    return p1.lanes == 64 && (p1.nbl == 2 || p1.nbl == 4) && (p1.rows == 1 || p1.rows == 2) && p2.nbl == 1 &&
+           p2.rows == 1 && (p2.lanes == 4 || p2.lanes == 8 || p2.lanes == 16);
+}
+
+template <int NBL, int R, int W2>
+void launch_pair3(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const int8_t* a_qs,
+                         const uint32_t* a_sd, const float* x) {
+    const int wgs2 = (int)j2.p.workgroups;
+    const dim3 grid((unsigned)(j1.p.workgroups + wgs2));
+    hipLaunchKernelGGL((k_gemv_pair<64, NBL, R, W2>), grid, dim3(256), 0, s, j1.a, a_qs, a_sd, j1.K, j1.nb,
+                       j1.p.groups, j2.a, x, j2.K, j2.nb, j2.p.groups, wgs2);
+}
+
+template <int NBL, int R>
+void launch_pair2(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const int8_t* a_qs,
+                         const uint32_t* a_sd, const float* x) {
+    if (j2.p.lanes == 4)
+        launch_pair3<NBL, R, 4>(j1, j2, s, a_qs, a_sd, x);
+    else if (j2.p.lanes == 8)
+        launch_pair3<NBL, R, 8>(j1, j2, s, a_qs, a_sd, x);
+    else
+        launch_pair3<NBL, R, 16>(j1, j2, s, a_qs, a_sd, x);
+}
+
+void launch_pair(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const int8_t* a_qs,
+                        const uint32_t* a_sd, const float* x) {
+    if (j1.p.nbl == 4) {
+        if (j1.p.rows == 2)
+            launch_pair2<4, 2>(j1, j2, s, a_qs, a_sd, x);
+        else
+            launch_pair2<4, 1>(j1, j2, s, a_qs, a_sd, x);
+    } else {
+        if (j1.p.rows == 2)
+            launch_pair2<2, 2>(j1, j2, s, a_qs, a_sd, x);
+        else
+            launch_pair2<2, 1>(j1, j2, s, a_qs, a_sd, x);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int q8_gemv_plan(int64_t total_rows, int64_t k, int rows_per_wave, int* lanes_per_row, int* rows_per_wave_out,
+                 int64_t* workgroups) {
+    if (total_rows < 0 || k <= 0 || (k % kQK) != 0) return Q8_ESHAPE;
+    if (rows_per_wave != 0 && rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4) return Q8_EINVAL;
+    const Plan p = make_plan(total_rows, (int)(k / kQK), rows_per_wave);
+    if (lanes_per_row) *lanes_per_row = p.lanes;
+    if (rows_per_wave_out) *rows_per_wave_out = p.rows;
+    if (workgroups) *workgroups = total_rows == 0 ? 0 : p.workgroups;
+    return Q8_OK;
+}
+
+// The grouped GEMV behind q8_gemv, q8_gemv_shared_multi and _ex; `counter`
+// names the entry point whose launch counter a launch adds to.
+static int gemv_multi(int counter, int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
+                      float* const* y, int rows_per_wave, void* stream) {
+    GemvJob j;
+    int rc = prepare_multi(m, W, a_qs, a_sd, y, rows_per_wave, j);
+    if (rc || j.empty) return rc;
+    launch_multi(j, (hipStream_t)stream, a_qs, a_sd);
     return q8h::launch_status(counter);
 }
 
@@ -365,26 +494,35 @@ int q8_gemv_shared_multi(int m, const q8_weights* const* W, const int8_t* a_qs, 
 }
 
 int q8_gemv_f32(const q8_weights* W, const float* x, float* y, void* stream) {
-    int rc = check_weights(W);
-    if (rc) return rc;
-    if (W->k > kMaxF32K) return Q8_ESHAPE;
-    if (x == nullptr || (y == nullptr && W->n > 0)) return Q8_EINVAL;
-    if (!q8h::aligned(x, 16) || !q8h::aligned(y, 4)) return Q8_EALIGN;
-    if (W->n == 0) return Q8_OK;
-    GemvArgs a;
-    for (int i = 0; i < kMaxMats; ++i) {
-        a.wq[i] = W->qs;
-        a.wd[i] = W->d;
-        a.y[i] = y;
-        a.off[i] = i == 0 ? 0 : INT64_MAX;
-    }
-    a.total = W->n;
-    a.safe_q = W->qs;
-    a.safe_d = W->d;
-    const int nb = (int)(W->k / kQK);
-    const Plan p = make_plan(W->n, nb, 0);
-    launch_m<false, true>(p, (hipStream_t)stream, a, nullptr, nullptr, x, (int)W->k, nb);
+    GemvJob j;
+    int rc = prepare_f32(W, x, y, j);
+    if (rc || j.empty) return rc;
+    launch_f32(j, (hipStream_t)stream, x);
     return q8h::launch_status(Q8_LAUNCH_GEMV_F32);
+}
+
+int q8_gemv_shared_multi_plus_f32(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
+                                  float* const* y, const q8_weights* Wx, const float* x, float* yx, void* stream) {
+    GemvJob j1, j2;
+    int rc = prepare_multi(m, W, a_qs, a_sd, y, 0, j1);
+    if (rc) return rc;
+    if ((rc = prepare_f32(Wx, x, yx, j2))) return rc;
+    const hipStream_t s = (hipStream_t)stream;
+    constexpr int ctr = Q8_LAUNCH_GEMV_SHARED_MULTI_PLUS_F32;
+    if (!j1.empty && !j2.empty && pair_supported(j1.p, j2.p)) {
+        launch_pair(j1, j2, s, a_qs, a_sd, x);
+        return q8h::launch_status(ctr);
+    }
+    // one part empty, or shapes without a pair kernel: the two kernels back to back
+    if (!j1.empty) {
+        launch_multi(j1, s, a_qs, a_sd);
+        if ((rc = q8h::launch_status(ctr))) return rc;
+    }
+    if (!j2.empty) {
+        launch_f32(j2, s, x);
+        if ((rc = q8h::launch_status(ctr))) return rc;
+    }
+    return Q8_OK;
 }
 
 int q8_gemv(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, float* y, void* stream) {

@@ -422,7 +422,8 @@ void q8_launch_counts_reset(void) {
 const char* q8_launch_counter_name(int id) {
     static const char* const names[Q8_LAUNCH_COUNTERS] = {
         "q8_quantize", "rmsnorm_quant", "swiglu_quant", "q8_gemv", "q8_gemv_shared_multi",
-        "q8_gemv_f32", "q8_gemm", "q8_gemm_shared_multi", "q4k_gemm", "q8_weights_repack"};
+        "q8_gemv_f32", "q8_gemm", "q8_gemm_shared_multi", "q4k_gemm", "q8_weights_repack",
+        "q8_gemv_shared_multi_plus_f32"};
     return (id >= 0 && id < Q8_LAUNCH_COUNTERS) ? names[id] : nullptr;
 }
 

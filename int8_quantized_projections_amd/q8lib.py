@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
             "q8_gemm_shared_multi": ([ci, ctypes.POINTER(wp), vp, vp, i64, ctypes.POINTER(vp), ctypes.POINTER(i64), vp],
                                      ci),
             "q8_weights_repack": ([vp, i64, i64, vp, vp, vp], ci),
+            "q8_gemv_shared_multi_plus_f32": ([ci, ctypes.POINTER(wp), vp, vp, ctypes.POINTER(vp), wp, vp, vp, vp], ci),
             "q8_launch_counts": ([ctypes.POINTER(i64), ci], ci),
             "q8_launch_counts_reset": ([], None),
             "q8_launch_counter_name": ([ci], ctypes.c_char_p),
@@ -277,6 +278,23 @@ def q8_gemv_shared_multi(Ws: list[Q8Weights], a_qs: torch.Tensor, a_sd: torch.Te
     _check(lib().q8_gemv_shared_multi_ex(m, wps, _ptr(a_qs), _ptr(a_sd), yps, rows_per_wave, _stream(a_qs.device)),
            "q8_gemv_shared_multi")
     return ys
+
+
+def q8_gemv_shared_multi_plus_f32(Ws: list[Q8Weights], a_qs: torch.Tensor, a_sd: torch.Tensor, Wx: Q8Weights,
+                                  x: torch.Tensor, ys=None, yx=None) -> tuple[list[torch.Tensor], torch.Tensor]:
+    """q8_gemv_shared_multi(Ws, a_qs, a_sd) and q8_gemv_f32(Wx, x) in one launch; returns (ys, yx)."""
+    m = len(Ws)
+    if ys is None:
+        ys = [torch.empty(W.n, dtype=torch.float32, device=a_qs.device) for W in Ws]
+    if yx is None:
+        yx = torch.empty(Wx.n, dtype=torch.float32, device=x.device)
+    structs = [W.struct() for W in Ws]
+    wps = (ctypes.POINTER(_Weights) * m)(*[ctypes.pointer(st) for st in structs])
+    yps = (ctypes.c_void_p * m)(*[_ptr(y) for y in ys])
+    wx = Wx.struct()
+    _check(lib().q8_gemv_shared_multi_plus_f32(m, wps, _ptr(a_qs), _ptr(a_sd), yps, ctypes.byref(wx), _ptr(x),
+                                               _ptr(yx), _stream(a_qs.device)), "q8_gemv_shared_multi_plus_f32")
+    return ys, yx
 
 
 def gemv_plan(total_rows: int, k: int, rows_per_wave: int = 0) -> dict:

@@ -222,3 +222,30 @@ def test_rejected_and_empty_calls_launch_nothing(L):
     assert L.q8_gemm(ctypes.byref(W1), f, f, 0, f, 8, None) == Q8_OK
     assert L.q8_weights_repack(f, 0, 64, f, f, None) == Q8_OK
     assert all(v == 0 for v in q8lib.launch_counts().values())
+
+
+def test_gemv_pair_rejects_before_launch(L):
+    """q8_gemv_shared_multi_plus_f32 validates both parts before launching anything."""
+    f = FAKE
+    W = q8lib._Weights(8, 64, ctypes.c_void_p(f), ctypes.c_void_p(f))
+    Wbig = q8lib._Weights(8, 8224, ctypes.c_void_p(f), ctypes.c_void_p(f))
+    W96 = q8lib._Weights(8, 96, ctypes.c_void_p(f), ctypes.c_void_p(f))
+    W0 = q8lib._Weights(0, 64, ctypes.c_void_p(f), ctypes.c_void_p(f))
+    wps = (ctypes.POINTER(q8lib._Weights) * 1)(ctypes.pointer(W))
+    w0 = (ctypes.POINTER(q8lib._Weights) * 1)(ctypes.pointer(W0))
+    ys = (ctypes.c_void_p * 1)(f)
+    fn = L.q8_gemv_shared_multi_plus_f32
+    L.q8_launch_counts_reset()
+    assert fn(0, wps, f, f, ys, ctypes.byref(W), f, f, None) == Q8_EINVAL          # m < 1
+    assert fn(1, wps, f, f, ys, None, f, f, None) == Q8_EINVAL                     # no f32 part
+    assert fn(1, wps, f, f, ys, ctypes.byref(W), None, f, None) == Q8_EINVAL       # no x
+    assert fn(1, wps, f, f, ys, ctypes.byref(Wbig), f, f, None) == Q8_ESHAPE       # f32 K > 8192
+    assert fn(1, wps, f, f, ys, ctypes.byref(W), f + 4, f, None) == Q8_EALIGN      # x not 16-byte aligned
+    assert fn(1, wps, f + 4, f, ys, ctypes.byref(W), f, f, None) == Q8_EALIGN      # a_qs not 16-byte aligned
+    assert fn(1, wps, None, f, ys, ctypes.byref(W), f, f, None) == Q8_EINVAL       # no activation
+    # grouped members must share K; the f32 part has its own K
+    two = (ctypes.POINTER(q8lib._Weights) * 2)(ctypes.pointer(W), ctypes.pointer(W96))
+    assert fn(2, two, f, f, (ctypes.c_void_p * 2)(f, f), ctypes.byref(W), f, f, None) == Q8_ESHAPE
+    # both parts empty: valid, nothing launched
+    assert fn(1, w0, f, f, ys, ctypes.byref(W0), f, f, None) == Q8_OK
+    assert all(v == 0 for v in q8lib.launch_counts().values())

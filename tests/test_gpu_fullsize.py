@@ -90,7 +90,9 @@ def test_decode_projection_set_full():
     W128, wq128, wd128 = workload_weights(wl, "W128")
     bq, bsd = q8lib.q8_quantize(up(x128), ROW)
     y128 = q8lib.q8_gemv(W128, bq, bsd)
-    y128f = q8lib.q8_gemv_f32(W128, up(x128).view(-1))  # as the benchmark's step runs it
+    y128f = q8lib.q8_gemv_f32(W128, up(x128).view(-1))
+    # as the benchmark's step runs them: both GEMVs in one launch
+    pys, py128 = q8lib.q8_gemv_shared_multi_plus_f32([ws[n][0] for n in names], aq, asd, W128, up(x128).view(-1))
     torch.cuda.synchronize()
     assert_rel(to_np(y), y_ref, 1e-5, "rmsnorm 1x7168")
     assert torch.equal(aq_f, aq2) and torch.equal(asd_f, asd2), "fused quantize differs from standalone"
@@ -99,11 +101,13 @@ def test_decode_projection_set_full():
         ref, norm = oracle.gemv(wq, wd, qo[0], do[0])
         assert_norm(to_np(out), ref, norm, 1e-5, f"gemv {n}")
         assert torch.equal(out, singles[n]), f"grouped {n} differs from its separate launch"
+        assert torch.equal(out, pys[names.index(n)]), f"paired {n} differs from the grouped launch"
     q1, d1, s1 = oracle.quantize(x128)
     assert np.array_equal(to_np(bq), q1.reshape(-1))
     ref, norm = oracle.gemv(wq128, wd128, q1[0], d1[0])
     assert_norm(to_np(y128), ref, norm, 1e-5, "gemv 4096x128")
     assert torch.equal(y128f, y128), "q8_gemv_f32 differs from q8_quantize + q8_gemv"
+    assert torch.equal(py128, y128), "the paired f32 GEMV differs from q8_quantize + q8_gemv"
     assert_norm(to_np(y128f), ref, norm, 1e-5, "gemv_f32 4096x128")
 
 

@@ -199,3 +199,45 @@ def test_gemv_f32_equals_quantize_then_gemv(N, K):
         qo, do, _ = oracle.quantize(x)
         ref, norm = oracle.gemv(wq, wd, qo[0], do[0])
         assert_norm(to_np(y), ref, norm, 1e-5, f"q8_gemv_f32 {N}x{K} vs oracle")
+
+
+# q8_gemv_shared_multi_plus_f32: (grouped member Ns, K) with (f32 part Nx, Kx), and the
+# launches it must make: one for the shapes with a pair kernel, two for the others
+# (grouped K <= 2048, f32 K > 512), one when a part is empty.
+PAIR_CASES = [
+    ([4096, 512, 512, 4096, 12288, 96], 7168, 4096, 128, 1),  # the decode projection set
+    ([300, 200], 3584, 100, 256, 1),
+    ([129], 2080, 33, 512, 1),
+    ([5, 0, 70], 4096, 7, 96, 1),
+    ([64], 1024, 64, 128, 2),
+    ([200, 100], 3584, 50, 2048, 2),
+    ([300], 3584, 0, 128, 1),
+    ([0, 0], 3584, 40, 128, 1),
+]
+
+
+def _weights_or_empty(n, K, stream):
+    W = weights(synth.normal((max(n, 1), K), stream=stream, std=0.02))[0]
+    return W if n else W.rows(0, 0)
+
+
+@pytest.mark.parametrize("Ns,K,Nx,Kx,launches", PAIR_CASES)
+def test_gemv_pair_bit_identical_to_separate_calls(Ns, K, Nx, Kx, launches):
+    Ws = [_weights_or_empty(n, K, 4700 + 7 * i + len(Ns)) for i, n in enumerate(Ns)]
+    Wx = _weights_or_empty(Nx, Kx, 4750 + Kx)
+    aq, asd = q8lib.q8_quantize(up(synth.normal((1, K), stream=4760 + K)), q8lib.LAYOUT_ROW)
+    for xh in (synth.normal((1, Kx), stream=4761 + Kx), edge_activation(Kx, Kx + 1)):
+        x = up(xh).view(-1)
+        ref_y = q8lib.q8_gemv_shared_multi(Ws, aq, asd)
+        ref_x = q8lib.q8_gemv_f32(Wx, x) if Nx else None
+        ys = [poisoned(max(W.n, 1), torch.float32, 0xFF)[: W.n] for W in Ws]
+        yx = poisoned(max(Nx, 1), torch.float32, 0xFF)[:Nx]
+        torch.cuda.synchronize()
+        q8lib.launch_counts_reset()
+        q8lib.q8_gemv_shared_multi_plus_f32(Ws, aq, asd, Wx, x, ys, yx)
+        torch.cuda.synchronize()
+        assert q8lib.launch_counts()["q8_gemv_shared_multi_plus_f32"] == launches
+        for i, (a, b) in enumerate(zip(ys, ref_y)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"member {i} of {Ns}x{K}"
+        if Nx:
+            assert torch.equal(yx.view(torch.int32), ref_x.view(torch.int32)), f"f32 part {Nx}x{Kx}"

@@ -5,12 +5,14 @@ per-token decode sequence.
 
 Every count below is predicted from the structure of the computation before
 anything runs, and the measured counters must equal it exactly:
-- the fused decode layer (H=7168) is rmsnorm_quant, one grouped GEMV over the
-  six K=7168 consumers and q8_gemv_f32 for the K=128 consumer: 3 launches;
-- the unfused layer is rmsnorm_quant, a grouped GEMV over the four
-  attention/gate consumers, two single GEMVs, q8_quantize and q8_gemv: 6;
-- the saving is therefore exactly 3 launches per layer, and both forms give
-  identical outputs.
+- the unfused decode layer (H=7168) is rmsnorm_quant, a grouped GEMV over the
+  four attention/gate consumers, two single GEMVs, q8_quantize and q8_gemv: 6;
+- the grouped layer is rmsnorm_quant, one grouped GEMV over the six K=7168
+  consumers and q8_gemv_f32 for the K=128 consumer: 3;
+- the paired layer is rmsnorm_quant and q8_gemv_shared_multi_plus_f32, both
+  GEMVs in one launch: 2;
+- the savings are therefore exactly 3 and 4 launches per layer, and all three
+  forms give identical outputs.
 Launches captured into a graph count once, at capture; replays count nothing
 and reproduce the eager results bit for bit, with eager work and
 synchronizations between the replays.
@@ -67,6 +69,12 @@ def fused_layer(ws, x, w, x128, B):
     q8lib.q8_gemv_f32(ws["W128"], x128, B.out["W128"])
 
 
+def paired_layer(ws, x, w, x128, B):
+    q8lib.rmsnorm_quant(x, w, EPS, ROW, B.y, B.aq, B.asd)
+    q8lib.q8_gemv_shared_multi_plus_f32([ws[n] for n in GROUP], B.aq, B.asd, ws["W128"], x128,
+                                        [B.out[n] for n in GROUP], B.out["W128"])
+
+
 def unfused_layer(ws, x, w, x128, B):
     q8lib.rmsnorm_quant(x, w, EPS, ROW, B.y, B.aq, B.asd)
     q8lib.q8_gemv_shared_multi([ws[n] for n in GROUP[:4]], B.aq, B.asd, [B.out[n] for n in GROUP[:4]])
@@ -77,36 +85,38 @@ def unfused_layer(ws, x, w, x128, B):
 
 
 FUSED = {"rmsnorm_quant": 1, "q8_gemv_shared_multi": 1, "q8_gemv_f32": 1}
+PAIRED = {"rmsnorm_quant": 1, "q8_gemv_shared_multi_plus_f32": 1}
 UNFUSED = {"rmsnorm_quant": 1, "q8_gemv_shared_multi": 1, "q8_gemv": 3, "q8_quantize": 1}
 
 
 def test_decode_launch_counts_match_model_arithmetic(decode):
     ws, x, w, x128 = decode
-    Bf, Bu = Buffers(ws), Buffers(ws)
+    Bf, Bp, Bu = Buffers(ws), Buffers(ws), Buffers(ws)
     torch.cuda.synchronize()
-    q8lib.launch_counts_reset()
-    for _ in range(LAYERS):
-        fused_layer(ws, x, w, x128, Bf)
-    fused = counts()
-    q8lib.launch_counts_reset()
-    for _ in range(LAYERS):
-        unfused_layer(ws, x, w, x128, Bu)
-    unfused = counts()
+    measured = {}
+    for name, layer, B in (("fused", fused_layer, Bf), ("paired", paired_layer, Bp), ("unfused", unfused_layer, Bu)):
+        q8lib.launch_counts_reset()
+        for _ in range(LAYERS):
+            layer(ws, x, w, x128, B)
+        measured[name] = counts()
     torch.cuda.synchronize()
-    assert fused == {k: LAYERS * v for k, v in FUSED.items()}
-    assert unfused == {k: LAYERS * v for k, v in UNFUSED.items()}
-    # the predicted saving, as a count: 3 launches per layer
-    assert sum(unfused.values()) - sum(fused.values()) == 3 * LAYERS
-    for a, b, n in zip(Bf.outputs(), Bu.outputs(), GROUP + ["W128"]):
+    assert measured["fused"] == {k: LAYERS * v for k, v in FUSED.items()}
+    assert measured["paired"] == {k: LAYERS * v for k, v in PAIRED.items()}
+    assert measured["unfused"] == {k: LAYERS * v for k, v in UNFUSED.items()}
+    # the predicted savings, as counts: 3 and 4 launches per layer
+    total = {k: sum(v.values()) for k, v in measured.items()}
+    assert total["unfused"] - total["fused"] == 3 * LAYERS
+    assert total["unfused"] - total["paired"] == 4 * LAYERS
+    for a, b, c, n in zip(Bf.outputs(), Bp.outputs(), Bu.outputs(), GROUP + ["W128"]):
         assert not torch.isnan(a).any(), n
-        assert torch.equal(a, b), f"{n}: the fused and unfused layers differ"
+        assert torch.equal(a, b) and torch.equal(a, c), f"{n}: the layer forms differ"
 
 
 def test_graph_capture_counts_once_and_replays_match_eager(decode):
     ws, x, w, x128 = decode
     # eager reference of the captured inputs
     Be = Buffers(ws)
-    fused_layer(ws, x, w, x128, Be)
+    paired_layer(ws, x, w, x128, Be)
     ref = Be.outputs()
     # other inputs for the eager work between replays
     x2 = up(synth.normal((1, H), stream=7301))
@@ -117,10 +127,10 @@ def test_graph_capture_counts_once_and_replays_match_eager(decode):
     g = torch.cuda.CUDAGraph()
     q8lib.launch_counts_reset()
     with torch.cuda.graph(g):
-        fused_layer(ws, x, w, x128, Bg)
-    assert counts() == FUSED, "capture records each launch once"
+        paired_layer(ws, x, w, x128, Bg)
+    assert counts() == PAIRED, "capture records each launch once"
     for i in range(3):
-        fused_layer(ws, x2, w, x128b, Bo)  # eager work between replays
+        paired_layer(ws, x2, w, x128b, Bo)  # eager work between replays
         torch.cuda.synchronize()
         for t in Bg.out.values():
             t.fill_(float("nan"))
@@ -131,7 +141,7 @@ def test_graph_capture_counts_once_and_replays_match_eager(decode):
             assert torch.equal(a, b), f"replay {i}: {n} differs from the eager result"
         assert torch.equal(Bg.aq, Be.aq) and torch.equal(Bg.asd, Be.asd), f"replay {i}: activation differs"
     # replays add nothing; the three eager layers add theirs
-    assert counts() == {k: 4 * v for k, v in FUSED.items()}
+    assert counts() == {k: 4 * v for k, v in PAIRED.items()}
     # the eager layers on the other inputs computed something else
     assert not torch.equal(Bo.out["Wq"], ref[0])
 
