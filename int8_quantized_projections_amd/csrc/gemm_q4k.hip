@@ -79,9 +79,14 @@ __device__ __forceinline__ void scale_min(uint32_t y, uint32_t z, uint32_t w, in
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_q4k(
     const int8_t* __restrict__ aq, const uint32_t* __restrict__ asd, const uint8_t* __restrict__ wblk,
     float* __restrict__ C, int64_t T, int64_t N, int K, int nb, int64_t ldc, int n_tiles, int64_t tiles) {
-    __shared__ __attribute__((aligned(16))) int8_t lds_a[2][kKT * kTileBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kBN * kQ4Row];
-    __shared__ __attribute__((aligned(16))) uint32_t lds_s[2][kKT * kGroup];
+    // one variable per buffer, so that reading one buffer need not wait for the
+    // copies into the other (see k_gemm)
+    __shared__ __attribute__((aligned(16))) int8_t lds_a0[kKT * kTileBytes], lds_a1[kKT * kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b0[kBN * kQ4Row], lds_b1[kBN * kQ4Row];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_s0[kKT * kGroup], lds_s1[kKT * kGroup];
+    auto lds_a = [&](int b) { return b ? lds_a1 : lds_a0; };
+    auto lds_b = [&](int b) { return b ? lds_b1 : lds_b0; };
+    auto lds_s = [&](int b) { return b ? lds_s1 : lds_s0; };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -142,13 +147,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const int c0 = st * kKT;
 #pragma unroll
         for (int it = 0; it < kKT * kTileBytes / 16 / 256; ++it)
-            lds_copy16(r_a, aoffs, (uint32_t)(c0 * kTileBytes + it * 4096), &lds_a[b][it * 4096 + wave * 1024]);
-        lds_copy4(r_s, soffs, (uint32_t)(c0 * kGroup * 4), &lds_s[b][wave * kGroup]);
+            lds_copy16(r_a, aoffs, (uint32_t)(c0 * kTileBytes + it * 4096), &lds_a(b)[it * 4096 + wave * 1024]);
+        lds_copy4(r_s, soffs, (uint32_t)(c0 * kGroup * 4), &lds_s(b)[wave * kGroup]);
         const uint32_t sb_off = (uint32_t)((st >> 1) * kQ4Block);
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             const int i = wave + 4 * k;
-            if (i < kCopies) lds_copy16(r_b, boff[decltype(half)::value][k], sb_off, &lds_b[b][i * 1024]);
+            if (i < kCopies) lds_copy16(r_b, boff[decltype(half)::value][k], sb_off, &lds_b(b)[i * 1024]);
         }
     };
 
@@ -156,9 +161,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     // 4*half .. 4*half+3 of the super-block.
     auto compute = [&](int buf, auto half) {
         constexpr int H = decltype(half)::value;
-        const int8_t* la = &lds_a[buf][0];
-        const uint8_t* lb = &lds_b[buf][bbase];
-        const uint32_t* ls = &lds_s[buf][0];
+        const int8_t* la = &lds_a(buf)[0];
+        const uint8_t* lb = &lds_b(buf)[bbase];
+        const uint32_t* ls = &lds_s(buf)[0];
         // this row's header: f16 d, f16 dmin, 12 scale bytes
         const uint4 hdr = *reinterpret_cast<const uint4*>(lb);
         const float dd = f16_value(hdr.x), dm = f16_value(hdr.x >> 16);
