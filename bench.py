@@ -127,7 +127,21 @@ def stats(ms_list):
     n = len(s)
     pick = lambda q: s[min(n - 1, max(0, int(round(q * (n - 1)))))]
     return {"median_us": pick(0.5) * 1e3, "p10_us": pick(0.1) * 1e3, "p90_us": pick(0.9) * 1e3,
-            "mean_us": sum(s) / n * 1e3, "reps": n}
+            "mean_us": sum(s) / n * 1e3, "reps": n, "reps_us": [round(v * 1e3, 2) for v in ms_list]}
+
+
+def device_info(torch):
+    """The GPU as the runtime reports it."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_GB": round(p.total_memory / 1e9, 1), "clock_kHz": getattr(p, "clock_rate", None)}
+
+
+def counted_launches(q8, fn):
+    """Kernel launches the library enqueues for one call of fn, by its launch counters."""
+    q8.launch_counts_reset()
+    fn()
+    return sum(q8.launch_counts().values())
 
 
 def time_each(D, fn, reps, warm=3):
@@ -290,8 +304,25 @@ def bench_decode(D, steps, warmup, log_reps):
                                     "frac_hbm": b / (st["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                     "launches_per_step": 0}
     del g
+    # the same step with one weight copy, resident in the 256 MB Infinity Cache ("warm")
+    gw = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw):
+        for i in range(steps):
+            for _, f in launches(0):
+                f()
+    gw.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    gw.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1)
+    del gw
     return {"ms_per_step": ms / steps, "step_bytes": step_bytes, "value_GBps": step_bytes * steps / (ms * 1e-3) / 1e9,
             "copies": ncopy, "components": comp, "launches_per_step": sum(counted.values()),
+            "launches_per_step_predicted": 2,
+            "warm": {"ms_per_step": warm_ms / steps, "GBps": step_bytes * steps / (warm_ms * 1e-3) / 1e9,
+                     "note": "one weight copy, resident in the Infinity Cache; not the headline"},
             "launch_counts_per_step": counted}
 
 
@@ -327,6 +358,7 @@ def bench_gemv2048(D, reps):
     gb = gemv_bytes(2048, 2048)
     fb = gemv_f32_bytes(2048, 2048)
     return {
+        "slice_launches": {"predicted": 1, "counted": counted_launches(q8, lambda: q8.q8_gemv_f32(Ws[0], x.view(-1), y))},
         "q8_gemv_f32_2048x2048": {**tf, "bytes": fb, "GBps": fb / tf["mean_us"] / 1e3,
                                   "frac_hbm": fb / tf["mean_us"] / 1e3 / HBM_PEAK_GBS, "launches": 1},
         "q8_quantize_2048": {**tq, "bytes": quant_bytes(1, 2048), "GBps": quant_bytes(1, 2048) / tq["mean_us"] / 1e3},
@@ -372,7 +404,9 @@ def bench_prefill_rms(D, reps):
                                                               [C[n] for n in names]), reps))
     n_all = sum(W.n for W in Ws.values())
     out[f"q8_gemm_shared_multi_qkv_{n_all}x{K}"] = gemm_entry(t, T, n_all, K)
-    out["slice_launches"] = 2
+    out["slice_launches"] = {"predicted": 2, "counted": counted_launches(q8, lambda: (
+        q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_PLANE64, y, pq, ps),
+        q8.q8_gemm_shared_multi([Ws[n] for n in names], pq, ps, T, [C[n] for n in names])))}
     out["slice_tok_per_s"] = T / ((prod_us + t["mean_us"]) * 1e-6)
     out["slice_tok_per_s_separate_gemms"] = T / ((prod_us + sep_us) * 1e-6)
     return out
@@ -400,6 +434,8 @@ def bench_prefill_swiglu(D, reps):
                                           "frac_hbm": b3 / t3["mean_us"] / 1e3 / HBM_PEAK_GBS}
     t2 = stats(time_each(D, lambda i: q8.q8_gemm(W, pq, ps, T, C), reps))
     out[f"q8_gemm_{N}x{K}"] = gemm_entry(t2, T, N, K)
+    out["slice_launches"] = {"predicted": 2, "counted": counted_launches(q8, lambda: (
+        q8.swiglu_quant(g, u, q8.LAYOUT_PLANE64, y, pq, ps), q8.q8_gemm(W, pq, ps, T, C)))}
     out["slice_tok_per_s"] = T / ((t["mean_us"] + t2["mean_us"]) * 1e-6)
     out["slice_tok_per_s_no_f32"] = T / ((t3["mean_us"] + t2["mean_us"]) * 1e-6)
     return out
@@ -417,17 +453,20 @@ def bench_prefill_q4k(D, reps):
                         reps))
     out = {"rmsnorm_quant_plane64_no_f32": {**t, "bytes": rms_bytes(T, K, 1) - T * K * 4}}
     total_us = t["mean_us"]
+    launches = counted_launches(q8, lambda: q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_PLANE64, None, pq, ps, f32=False))
     for name in ("Wg", "Wu"):
         blocks = D.upload(synth.q4k_tensor("prefill_q4k", name))
         W = q8.Q4KWeights(blocks, K)
         C = torch.empty((T, W.n), device=D.dev)
         tg = stats(time_each(D, lambda i: q8.q4k_gemm(W, pq, ps, T, C), reps))
+        launches += counted_launches(q8, lambda: q8.q4k_gemm(W, pq, ps, T, C))
         e = gemm_entry(tg, T, W.n, K)
         e["min_bytes"] = T * K + (T // 64 + 1) * (K // 32) * 256 + blocks.numel() + T * W.n * 4
         e["GBps_min_bytes"] = e["min_bytes"] / tg["mean_us"] / 1e3
         out[f"q4k_gemm_{name}_{W.n}x{K}"] = e
         total_us += tg["mean_us"]
         del W, C, blocks
+    out["slice_launches"] = {"predicted": 3, "counted": launches}
     out["slice_tok_per_s"] = T / (total_us * 1e-6)
     return out
 
@@ -452,6 +491,8 @@ def bench_lm_head(D, reps):
     gb = gemv_bytes(N, K)
     out[f"q8_gemv_{N}x{K}"] = {**tg, "bytes": gb, "GBps": gb / tg["mean_us"] / 1e3,
                                 "frac_hbm": gb / tg["mean_us"] / 1e3 / HBM_PEAK_GBS}
+    out["t1_slice_launches"] = {"predicted": 2, "counted": counted_launches(q8, lambda: (
+        q8.rmsnorm_quant(x1, w, EPS, q8.LAYOUT_ROW, y1, aq, asd), q8.q8_gemv(Ws[0], aq, asd, logits)))}
     out["t1_slice_tok_per_s"] = 1.0 / ((t["mean_us"] + tg["mean_us"]) * 1e-6)
     T = 512
     y512 = torch.empty_like(x512)
@@ -462,6 +503,8 @@ def bench_lm_head(D, reps):
                                         "GBps": rms_bytes(T, K, 1) / t["mean_us"] / 1e3}
     t2 = stats(time_each(D, lambda i: q8.q8_gemm(Ws[i % n], pq, ps, T, C), max(3, reps // 2)))
     out[f"q8_gemm_{N}x{K}_T512"] = gemm_entry(t2, T, N, K)
+    out["t512_slice_launches"] = {"predicted": 2, "counted": counted_launches(q8, lambda: (
+        q8.rmsnorm_quant(x512, w, EPS, q8.LAYOUT_PLANE64, y512, pq, ps), q8.q8_gemm(Ws[0], pq, ps, T, C)))}
     out["t512_slice_tok_per_s"] = T / ((t["mean_us"] + t2["mean_us"]) * 1e-6)
     return out
 
@@ -500,11 +543,23 @@ def cpu_baseline(budget_s=10.0, max_steps=100000):
         k += 1
     dt = time.perf_counter() - t0
     step_bytes = sum(decode_step_bytes().values())
-    return {"value": step_bytes * k / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+    cores = oracle.num_threads()
+    # the same steps on one thread, a shorter sample (the results do not depend on the thread count)
+    oracle.set_threads(1)
+    t1 = time.perf_counter()
+    k1 = 0
+    while k1 < max_steps and (time.perf_counter() - t1) < budget_s / 4:
+        step()
+        k1 += 1
+    dt1 = time.perf_counter() - t1
+    oracle.set_threads(cores)
+    return {"value": step_bytes * k / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{k} full decode steps (rmsnorm + quantize, the six K=7168 GEMVs, quantize + GEMV "
                       f"for K=128; oracle references, f64) in {dt:.1f} s; "
                       "weights quantized once beforehand, untimed",
-            "ms_per_step": dt / k * 1e3}
+            "ms_per_step": dt / k * 1e3,
+            "single_thread": {"value": step_bytes * k1 / dt1 / 1e9, "unit": "GB/s", "cores": 1,
+                              "ms_per_step": dt1 / k1 * 1e3, "steps": k1}}
 
 
 def hbm_reference(D, mib=1024, reps=5):
@@ -609,11 +664,14 @@ def main():
                             "over N=4096/512/512/4096/12288/96 (K=7168) and the N=4096 K=128 GEMV, whose f32 "
                             "activation is quantized in the launch",
                    "launches_per_step": dec["launches_per_step"],
+                   "launches_per_step_predicted": dec["launches_per_step_predicted"],
                    "launch_counts_per_step": dec["launch_counts_per_step"], "weight_copies": dec["copies"],
                    "timing": "HIP graph of all timed steps, HIP events around the replay"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "hbm_reference": hbm,
+        "device": device_info(torch),
+        "decode_warm": dec["warm"],
         "components": dec["components"],
         "per_config": per,
     }

@@ -65,6 +65,7 @@ def lib():
             "q8o_gemm_full": ([vp, vp, i64, i64, vp, vp, i64, vp, vp], None),
             "q8o_block_isums": ([vp, i64, i64, vp, i64, vp], None),
             "q8o_num_threads": ([], ctypes.c_int),
+            "q8o_set_threads": ([ctypes.c_int], None),
             "q4ko_scale_min": ([vp, ctypes.c_int, vp, vp], None),
             "q4ko_decode": ([vp, i64, i64, vp, vp, vp, vp, vp], None),
             "q4ko_dequant_f64": ([vp, i64, i64, vp], None),
@@ -86,6 +87,11 @@ def _c(a: np.ndarray, dtype) -> np.ndarray:
 
 def num_threads() -> int:
     return lib().q8o_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the following calls (results do not depend on it)."""
+    lib().q8o_set_threads(n)
 
 
 # -- f16 ---------------------------------------------------------------------

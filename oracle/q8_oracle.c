@@ -25,6 +25,15 @@ int q8o_num_threads(void) {
 #endif
 }
 
+/* Threads the following oracle calls use (timing only; results do not depend on it). */
+void q8o_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------
  * IEEE-754 binary16 conversion, written from the format definition:
  * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; subnormals have

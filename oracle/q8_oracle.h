@@ -71,6 +71,7 @@ void q4ko_gemm_full(const uint8_t* blocks, int64_t N, int64_t K, const int8_t* a
                     const int16_t* assum, int64_t T, double* ref, double* norm);
 
 int q8o_num_threads(void);
+void q8o_set_threads(int n);
 
 #ifdef __cplusplus
 }
