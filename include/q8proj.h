@@ -181,8 +181,10 @@ int swiglu_quant(const float* gate, const float* up, float* y, int64_t rows, int
  * isum[n,b] = sum_{j<32} qw[n,32b+j] * qa[32b+j] (exact int32).
  * W: host pointer to the weight descriptor. a_qs, a_sd: one ROW-layout
  * activation row of width W->k. y: [N] f32.
- * The number of lanes per row follows K/32 and the rows per wave follow N
- * (a dispatch threshold); every variant gives bit-identical y.
+ * The number of lanes per row follows K/32. The rows per wave are 1 while the
+ * activation fits a wave's registers (K <= 8192); for wider K they follow N
+ * (a dispatch threshold: 2 from 2048 row slots, 4 from 16384). Every variant
+ * gives bit-identical y.
  */
 int q8_gemv(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, float* y, void* stream);
 

@@ -82,6 +82,7 @@ __device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __r
                                          int nb, int64_t groups, int64_t wave_id, int64_t nwaves) {
     constexpr int G = kWave / W;  // row slots per wave
     constexpr int CH = W * NBL;   // blocks per chunk
+    constexpr int kSeq = NBL < 2 ? NBL : 2;  // block columns per load step
     const int lane = threadIdx.x & (kWave - 1);
     const int slot = lane / W, u = lane % W;
     const int nchunks = (nb + CH - 1) / CH;
@@ -154,40 +155,51 @@ __device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __r
         for (int ch = 0; ch < nch; ++ch) {
             if constexpr (!F32A)
                 if (nchunks > 1) load_act(ch);
-            uint4 w0[R][NBL], w1[R][NBL];
-            uint16_t dw[R][NBL];
             bool inb[NBL];
 #pragma unroll
             for (int j = 0; j < NBL; ++j) inb[j] = ch * CH + u + j * W < nb;
+            // Block columns in steps of kSeq: a step's loads are issued, then consumed,
+            // before the next step's loads. Fewer bytes in flight per wave measured
+            // faster (5.24 -> 5.5 TB/s on the decode set): the requests of all waves
+            // then fall into fewer, denser address ranges. The per-row order of the
+            // accumulation is unchanged (j ascending).
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
+            for (int j0 = 0; j0 < NBL; j0 += kSeq) {
+                uint4 w0[R][kSeq], w1[R][kSeq];
+                uint16_t dw[R][kSeq];
 #pragma unroll
-                for (int j = 0; j < NBL; ++j) {
-                    const int b = ch * CH + u + j * W;
-                    const int bc = b < nb ? b : nb - 1;
-                    w0[r][j] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK);
-                    w1[r][j] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK + 16);
-                    dw[r][j] = drow[r][bc];
+                for (int r = 0; r < R; ++r) {
+#pragma unroll
+                    for (int jj = 0; jj < kSeq; ++jj) {
+                        const int b = ch * CH + u + (j0 + jj) * W;
+                        const int bc = b < nb ? b : nb - 1;
+                        w0[r][jj] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK);
+                        w1[r][jj] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK + 16);
+                        dw[r][jj] = drow[r][bc];
+                    }
                 }
-            }
-            if constexpr (F32A && decltype(first)::value) {
-                __builtin_amdgcn_sched_barrier(0);  // the weight loads above are issued before this waits on x
+                if constexpr (F32A && decltype(first)::value) {
+                    if (j0 == 0) {
+                        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < NBL; ++j) {
-                    uint32_t dbits;
-                    quantize_lane32(xv[j], a0[j], a1[j], dbits);
-                    da[j] = f16_value(dbits);
+                        for (int j = 0; j < NBL; ++j) {
+                            uint32_t dbits;
+                            quantize_lane32(xv[j], a0[j], a1[j], dbits);
+                            da[j] = f16_value(dbits);
+                        }
+                    }
                 }
-            }
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
+                for (int r = 0; r < R; ++r) {
 #pragma unroll
-                for (int j = 0; j < NBL; ++j) {
-                    // blocks past K (a function of K only) add an exact zero
-                    const int isum = dot32(w0[r][j], w1[r][j], a0[j], a1[j]);
-                    const float sc = inb[j] ? f16_value(dw[r][j]) * da[j] : 0.0f;
-                    acc[r] = fmaf((float)isum, sc, acc[r]);
+                    for (int jj = 0; jj < kSeq; ++jj) {
+                        const int j = j0 + jj;
+                        const int isum = dot32(w0[r][jj], w1[r][jj], a0[j], a1[j]);
+                        const float sc = inb[j] ? f16_value(dw[r][jj]) * da[j] : 0.0f;
+                        acc[r] = fmaf((float)isum, sc, acc[r]);
+                    }
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
@@ -248,14 +260,23 @@ Plan make_plan(int64_t total, int nb, int force_rows) {
     const int64_t per_lane = (nb + p.lanes - 1) / p.lanes;
     p.nbl = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : 4;
     const int64_t slots = q8h::ceil_div(total, kWave / p.lanes);
-    // [P1] s2.3: several rows per wave reuse the activation but divide the
-    // grid; only take them when the grid stays large (threshold re-derived for
-    // 256 CUs: two rows per wave from 2048 row slots on; four rows per wave
-    // measured no faster and need 228 VGPRs, so they are only used on request).
+    // [P1] s2.3: several rows per wave share one load of the activation but
+    // divide the grid. Here the activation stays in a wave's registers for the
+    // whole launch when K fits one chunk (64 lanes x 4 blocks, K <= 8192); then
+    // extra rows only add loads in flight. One row per wave measured best, or
+    // within 3% of the best, at every shape of 30 MB or more from N=1024 to
+    // 152064 (decode set: 29.9 vs 32.5 us); launches under 10 us vary by up to
+    // 20% either way without a trend. Wider K
+    // reloads the activation chunks per row group, and there the rows per wave
+    // follow N: 1 below 2048 row slots, 2 below 16384, 4 from there on
+    // (K=18944, N=65536: 5.30 / 5.72 / 5.91 TB/s for 1 / 2 / 4).
+    const int64_t nchunks = q8h::ceil_div(nb, (int64_t)p.lanes * p.nbl);
     if (force_rows > 0)
         p.rows = force_rows;
+    else if (nchunks == 1)
+        p.rows = 1;
     else
-        p.rows = slots >= 2048 ? 2 : 1;
+        p.rows = slots >= 16384 ? 4 : slots >= 2048 ? 2 : 1;
     p.groups = q8h::ceil_div(slots, p.rows);
     const int64_t waves = p.groups < kMaxWaves ? p.groups : kMaxWaves;
     p.workgroups = q8h::ceil_div(waves, kWavesPerWg);
@@ -425,8 +446,12 @@ bool pair_supported(const Plan& p1, const Plan& p2) {
 template <int NBL, int R, int W2>
 void launch_pair3(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const int8_t* a_qs,
                          const uint32_t* a_sd, const float* x) {
+    // the grouped part is persistent: give it the resident slots the f32 part leaves,
+    // so that no workgroup of it starts late (a tail with few waves in flight)
     const int wgs2 = (int)j2.p.workgroups;
-    const dim3 grid((unsigned)(j1.p.workgroups + wgs2));
+    const int64_t cap = kMaxWaves / kWavesPerWg - wgs2;
+    const int64_t wgs1 = j1.p.workgroups < cap ? j1.p.workgroups : (cap > 0 ? cap : 1);
+    const dim3 grid((unsigned)(wgs1 + wgs2));
     hipLaunchKernelGGL((k_gemv_pair<64, NBL, R, W2>), grid, dim3(256), 0, s, j1.a, a_qs, a_sd, j1.K, j1.nb,
                        j1.p.groups, j2.a, x, j2.K, j2.nb, j2.p.groups, wgs2);
 }

@@ -161,17 +161,23 @@ def test_gemv_lanes_follow_k(L, nb, lanes):
 
 
 def test_gemv_rows_per_wave_threshold(L):
-    # [P1] s2.3: several rows per wave only when N leaves a large grid
-    assert q8lib.gemv_plan(96, 7168)["rows_per_wave"] == 1
-    assert q8lib.gemv_plan(2047, 7168)["rows_per_wave"] == 1
-    assert q8lib.gemv_plan(2048, 7168)["rows_per_wave"] == 2
-    assert q8lib.gemv_plan(4095, 7168)["rows_per_wave"] == 2
-    assert q8lib.gemv_plan(12288, 7168)["rows_per_wave"] == 2
+    # [P1] s2.3, re-derived for this kernel: while the activation fits a wave's registers
+    # (one chunk of 64 lanes x 4 blocks, K <= 8192) one row per wave, whatever N
+    for n in (96, 2047, 2048, 12288, 21600, 152064):
+        assert q8lib.gemv_plan(n, 7168)["rows_per_wave"] == 1
+    assert q8lib.gemv_plan(100000, 8192)["rows_per_wave"] == 1
+    # wider K re-reads the activation per row group: several rows per wave, by N
+    assert q8lib.gemv_plan(2047, 8224)["rows_per_wave"] == 1
+    assert q8lib.gemv_plan(2048, 8224)["rows_per_wave"] == 2
+    assert q8lib.gemv_plan(16383, 18944)["rows_per_wave"] == 2
+    assert q8lib.gemv_plan(16384, 18944)["rows_per_wave"] == 4
+    assert q8lib.gemv_plan(65536, 14336)["rows_per_wave"] == 4
+    # forced variants (tests and measurements)
     assert q8lib.gemv_plan(12288, 7168, rows_per_wave=4)["rows_per_wave"] == 4
+    assert q8lib.gemv_plan(4096, 18944, rows_per_wave=1)["rows_per_wave"] == 1
     # narrow rows share a wave: K=128 puts 16 rows in a wave, so 4096 rows give 256 slots
     p = q8lib.gemv_plan(4096, 128)
     assert p["lanes_per_row"] == 4 and p["rows_per_wave"] == 1
-    assert q8lib.gemv_plan(4096, 7168, rows_per_wave=1)["rows_per_wave"] == 1
     assert q8lib.gemv_plan(0, 7168)["workgroups"] == 0
     # the grid never exceeds the persistent cap, and covers small N fully
     assert q8lib.gemv_plan(152064, 3584)["workgroups"] == 4096 // 4

@@ -30,7 +30,9 @@ def run_gemv(W, aq, asd, rows_per_wave=0):
 
 # K around the lane-count boundaries (32/64/65 blocks), N around the row-group sizes
 CASES = [(1, 32), (3, 128), (5, 1024), (95, 2048), (96, 2080), (97, 3584), (1023, 1024), (1025, 7168),
-         (4097, 128), (7, 18944), (130, 960), (4096, 2048)]
+         (4097, 128), (7, 18944), (130, 960), (4096, 2048),
+         # K past one register chunk (8192): the automatic dispatch takes 2 and 4 rows per wave
+         (2048, 8224), (16390, 8224)]
 
 
 @pytest.mark.parametrize("N,K", CASES)
@@ -45,7 +47,7 @@ def test_gemv_matches_oracle(N, K):
     assert_norm(to_np(y), ref, norm, 1e-5, f"gemv {N}x{K}")
 
 
-@pytest.mark.parametrize("N,K", [(1025, 7168), (4097, 128), (96, 2080), (33, 18944)])
+@pytest.mark.parametrize("N,K", [(1025, 7168), (4097, 128), (96, 2080), (33, 18944), (2048, 8224), (16390, 8224)])
 def test_gemv_variants_bit_identical(N, K):
     x = synth.normal((1, K), stream=4100 + K)
     Wf = synth.normal((N, K), stream=4101, std=0.02)
