@@ -326,7 +326,7 @@ void q8o_block_isums(const int8_t* wq, int64_t N, int64_t K, const int8_t* aq, i
 }
 
 /* ------------------------------------------------------------------------
- * q4_K weights ([P3] s2, "the dequant-at-mma-time principle", and spec point
+ * q4_K weights ([P3] s2, on dequantizing at matrix time, and spec point
  * 1): a super-block of 256 values in 144 bytes -- f16 d at +0, f16 dmin at +2,
  * 12 bytes of packed 6-bit sub-block scales and mins at +4, 128 bytes of
  * 4-bit values at +16. Sub-block s (values 32s..32s+31, s = 0..7) takes value
