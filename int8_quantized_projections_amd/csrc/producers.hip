@@ -20,6 +20,31 @@ namespace {
 
 enum Dst : int { kDstNone = 0, kDstRow = 1, kDstPlane = 2 };
 
+// Streaming accesses: the non-temporal bit, so the line does not displace
+// others from L2 and the MALL. Measured per stream, not applied wholesale:
+// - every f32 output y and the PLANE64 tile stores: 5.1 -> 5.4 TB/s on the
+//   3325x18944 swiglu_quant with the plane, 3.2 -> 3.6 on the 3325x18944
+//   rmsnorm_quant, and never slower;
+// - the gate and up inputs of swiglu_quant (row layout 5.3 -> 6.1 TB/s);
+// - not the single input of q8_quantize or rmsnorm_quant: there they measured
+//   slower (rmsnorm_quant 3325x3584, 21 -> 25 us), as a row that the previous
+//   kernel just wrote is often still in the MALL;
+// - not the RMSNorm weight row, which every row reads.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(float* p, const float4& v) {
+    const f32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ void store_stream(void* p, const uint4& v) {
+    const u32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
+
 // Write this lane's 4 quantized values (and, from the group's first lane,
 // the block's scale word) for element e..e+3 of chunk c of row t.
 template <int D>
@@ -37,10 +62,11 @@ __device__ __forceinline__ void store_quant(const Quant8& r, int64_t t, int c, i
 // ---------------------------------------------------------------------------
 // Element-wise producers (quantize of x, or swiglu then quantize). A unit is
 // 8 consecutive blocks of one row = 256 floats = one float4 per lane. Each
-// wave does kUnr units, issuing all loads before any math; rows are padded to
-// 64 for PLANE64.
+// wave does kUnr units, one load step at a time; rows are padded to 64 for
+// PLANE64.
 // ---------------------------------------------------------------------------
 constexpr int kUnr = 4;
+constexpr int kSeq = 1;  // units per load step
 constexpr int kWavesPerWg = 4;
 
 template <int D, bool SWIGLU>
@@ -58,13 +84,9 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sub = lane & 7;
     const int64_t first = (L * kWavesPerWg + wave) * kUnr;
-    float4 v[kUnr], w[kUnr];
     int blk[kUnr];
     int64_t trow[kUnr];
     bool live[kUnr];
-    // Unconditional loads from clamped, always-valid addresses (a load inside a
-    // divergent branch serialises the stream); padded rows read row 0 and are
-    // zeroed at use.
 #pragma unroll
     for (int u = 0; u < kUnr; ++u) {
         const int64_t un = first + u < units ? first + u : units - 1;  // wave-uniform
@@ -80,10 +102,6 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
         blk[u] = (int)col * 8 + (lane >> 3);
         if (first + u >= units) blk[u] = nb;  // past the end: no output
         live[u] = trow[u] < rows;
-        const int bc = blk[u] < nb ? blk[u] : nb - 1;
-        const int64_t off = (live[u] ? trow[u] : 0) * K + (int64_t)bc * kQK + sub * 4;
-        v[u] = *reinterpret_cast<const float4*>(a + off);
-        if constexpr (SWIGLU) w[u] = *reinterpret_cast<const float4*>(b + off);
     }
     // PLANE64: this workgroup covers rows 16k..16k+15 of one 64-row group at one
     // 8-chunk column, i.e. a 512-byte slice of each of 8 tiles. The quantized
@@ -92,36 +110,60 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
     constexpr int kCs = kSlice * 8 + 8;  // words per chunk slice, padded against bank conflicts
     __shared__ __attribute__((aligned(16))) uint32_t pq[D == kDstPlane ? 8 * kCs : 1];
     __shared__ uint32_t psd[D == kDstPlane ? 8 * kSlice : 1];
+    // The units go in steps of kSeq: a step's loads are issued, then its math
+    // and stores run. One unit per step measured as fast as issuing all kUnr
+    // units' loads first (within 1-3%), with fewer registers live.
 #pragma unroll
-    for (int u = 0; u < kUnr; ++u) {
-        if (blk[u] >= nb) continue;  // whole 8-lane groups drop out together
-        if constexpr (SWIGLU) {
-            // [P2] s3.2: silu(g) * u = g / (1 + e^-g) * u, with the hardware exp2 and
-            // reciprocal (each within about an ulp; the f32 output is checked to 1e-5).
-            float4 o;
-            o.x = v[u].x * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].x)) * w[u].x;
-            o.y = v[u].y * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].y)) * w[u].y;
-            o.z = v[u].z * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].z)) * w[u].z;
-            o.w = v[u].w * __builtin_amdgcn_rcpf(1.0f + __expf(-v[u].w)) * w[u].w;
-            if (y != nullptr && live[u])  // y == NULL: quantized output only
-                *reinterpret_cast<float4*>(y + trow[u] * K + (int64_t)blk[u] * kQK + sub * 4) = o;
-            v[u] = o;
-        }
-        if constexpr (D != kDstNone) {
-            // padded rows (which loaded row 0) quantize a zero block: all bytes zero
-            const Quant8 r = quantize_block8(live[u] ? v[u] : make_float4(0.f, 0.f, 0.f, 0.f));
-            if constexpr (D == kDstPlane) {
-                const int rs = wave * kUnr + u;  // row in the slice
-                const int rt = (int)(trow[u] & 63);  // row in the tile (selects the half swizzle)
-                const int e = sub * 4;
-                const int h = ((e >> 4) ^ (rt >> 2) ^ (rt >> 3)) & 1;
-                const int cl = lane >> 3;  // chunk in the column
-                pq[cl * kCs + rs * 8 + h * 4 + ((e & 15) >> 2)] = r.qs4;
-                if (sub == 0) psd[cl * kSlice + rs] = r.sd;
-            } else {
-                store_quant<D>(r, trow[u], blk[u], sub * 4, K, nb, qs, sd);
+    for (int u0 = 0; u0 < kUnr; u0 += kSeq) {
+        float4 v[kSeq], w[kSeq];
+        // Unconditional loads from clamped, always-valid addresses (a load inside a
+        // divergent branch serialises the stream); padded rows read row 0 and are
+        // zeroed at use.
+#pragma unroll
+        for (int i = 0; i < kSeq; ++i) {
+            const int u = u0 + i;
+            const int bc = blk[u] < nb ? blk[u] : nb - 1;
+            const int64_t off = (live[u] ? trow[u] : 0) * K + (int64_t)bc * kQK + sub * 4;
+            if constexpr (SWIGLU) {  // two input streams: both read as streaming
+                v[i] = load_stream(a + off);
+                w[i] = load_stream(b + off);
+            } else {  // one stream: ordinary loads measured faster
+                v[i] = *reinterpret_cast<const float4*>(a + off);
             }
         }
+#pragma unroll
+        for (int i = 0; i < kSeq; ++i) {
+            const int u = u0 + i;
+            if (blk[u] >= nb) continue;  // whole 8-lane groups drop out together
+            if constexpr (SWIGLU) {
+                // [P2] s3.2: silu(g) * u = g / (1 + e^-g) * u, with the hardware exp2 and
+                // reciprocal (each within about an ulp; the f32 output is checked to 1e-5).
+                float4 o;
+                o.x = v[i].x * __builtin_amdgcn_rcpf(1.0f + __expf(-v[i].x)) * w[i].x;
+                o.y = v[i].y * __builtin_amdgcn_rcpf(1.0f + __expf(-v[i].y)) * w[i].y;
+                o.z = v[i].z * __builtin_amdgcn_rcpf(1.0f + __expf(-v[i].z)) * w[i].z;
+                o.w = v[i].w * __builtin_amdgcn_rcpf(1.0f + __expf(-v[i].w)) * w[i].w;
+                if (y != nullptr && live[u])  // y == NULL: quantized output only
+                    store_stream(y + trow[u] * K + (int64_t)blk[u] * kQK + sub * 4, o);
+                v[i] = o;
+            }
+            if constexpr (D != kDstNone) {
+                // padded rows (which loaded row 0) quantize a zero block: all bytes zero
+                const Quant8 r = quantize_block8(live[u] ? v[i] : make_float4(0.f, 0.f, 0.f, 0.f));
+                if constexpr (D == kDstPlane) {
+                    const int rs = wave * kUnr + u;  // row in the slice
+                    const int rt = (int)(trow[u] & 63);  // row in the tile (selects the half swizzle)
+                    const int e = sub * 4;
+                    const int h = ((e >> 4) ^ (rt >> 2) ^ (rt >> 3)) & 1;
+                    const int cl = lane >> 3;  // chunk in the column
+                    pq[cl * kCs + rs * 8 + h * 4 + ((e & 15) >> 2)] = r.qs4;
+                    if (sub == 0) psd[cl * kSlice + rs] = r.sd;
+                } else {
+                    store_quant<D>(r, trow[u], blk[u], sub * 4, K, nb, qs, sd);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (D == kDstPlane) {
         __syncthreads();
@@ -135,7 +177,7 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
         const int c = (int)col * 8 + cl;
         if (c < nb) {
             const uint4 v4 = *reinterpret_cast<const uint4*>(&pq[cl * kCs + (tid & 31) * 4]);
-            *reinterpret_cast<uint4*>(qs + (g * nb + c) * kTileBytes + r0 * 32 + (tid & 31) * 16) = v4;
+            store_stream(qs + (g * nb + c) * kTileBytes + r0 * 32 + (tid & 31) * 16, v4);
         }
         if (tid < 8 * kSlice) {
             const int c2 = (int)col * 8 + tid / kSlice;
@@ -221,7 +263,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_rmsnorm(const float* __restrict_
             o.y = v[k].y * scale * wv[k].y;
             o.z = v[k].z * scale * wv[k].z;
             o.w = v[k].w * scale * wv[k].w;
-            if (y4 != nullptr && live && idx < n4) y4[idx] = o;
+            if (y4 != nullptr && live && idx < n4) store_stream(reinterpret_cast<float*>(y4 + idx), o);
             v[k] = o;  // zero for padded rows and past K
         }
         if constexpr (D != kDstNone) {
@@ -260,7 +302,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_rmsnorm(const float* __restrict_
                 o.y = a.y * scale * wq.y;
                 o.z = a.z * scale * wq.z;
                 o.w = a.w * scale * wq.w;
-                if (y4 != nullptr) y4[idx] = o;
+                if (y4 != nullptr) store_stream(reinterpret_cast<float*>(y4 + idx), o);
             }
             if constexpr (D != kDstNone) {
                 const int c = idx >> 3;
