@@ -2,11 +2,12 @@
 """Benchmark of the Q8_0 projection path on one MI355X.
 
 Headline (one JSON line on stdout): the decode projection set at batch 1,
-H=7168 -- rmsnorm_quant (ROW) whose quantized activation feeds every K=7168
-consumer (N=4096/512/512/4096 plus N=12288 and N=96) in one grouped
-q8_gemv_shared_multi launch, then q8_quantize of a K=128 vector feeding
-q8_gemv N=4096 K=128. One step is those four launches; `value` is the step's
-algorithmic HBM bytes per second.
+H=7168 -- rmsnorm_quant (ROW) of the row, whose quantized activation feeds
+every K=7168 consumer (N=4096/512/512/4096 plus N=12288 and N=96), and the
+N=4096 K=128 GEMV on a second f32 vector, quantized in the launch. One step is
+one launch of rmsnorm_quant_gemv_shared_multi_plus_f32; `value` is the step's
+algorithmic HBM bytes per second. The same work as two launches (rmsnorm_quant,
+then q8_gemv_shared_multi_plus_f32) and as six is timed beside it.
 Weights rotate over enough distinct copies (>= 1 GB) that no step finds its
 weights in the 256 MB Infinity Cache or the L2s. The steps are captured once
 in a HIP graph and replayed; inputs are resident in HBM before timing.
@@ -188,16 +189,19 @@ DEC_N = {"Wq": 4096, "Wk": 512, "Wv": 512, "Wg": 4096, "W12288": 12288, "W96": 9
 DEC_GROUP = ("Wq", "Wk", "Wv", "Wg", "W12288", "W96")  # every consumer of the normed activation
 
 
+def decode_pair_bytes():
+    """The grouped GEMV over the six K=7168 consumers (one read of the q8_0 activation) and
+    the K=128 GEMV, its f32 activation quantized in the launch."""
+    return decode_grouped_bytes() + gemv_f32_bytes(4096, 128)
+
+
 def decode_step_bytes():
+    """The whole step in one launch: x and w read, y and the q8_0 activation written once,
+    every weight byte and output once. The grouped GEMV reads its activation from LDS, so
+    the pair's activation read is not counted."""
     H = 7168
-    grouped = sum(gemv_bytes(DEC_N[n], H) for n in DEC_GROUP) - (len(DEC_GROUP) - 1) * (H + (H // 32) * 4)
-    parts = {
-        "rmsnorm_quant_row": rms_bytes(1, H),
-        # the grouped GEMV over the six K=7168 consumers and the K=128 GEMV (its f32
-        # activation quantized in the launch), in one launch
-        "q8_gemv_shared_multi_plus_f32": grouped + gemv_f32_bytes(4096, 128),
-    }
-    return parts
+    return {"rmsnorm_quant_gemv_shared_multi_plus_f32":
+            rms_bytes(1, H) + decode_pair_bytes() - (H + (H // 32) * 4)}
 
 
 def decode_grouped_bytes():
@@ -226,17 +230,21 @@ def bench_decode(D, steps, warmup, log_reps):
     def launches(c):
         S = sets[c % ncopy]
         return [
-            ("rmsnorm_quant_row", lambda: q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_ROW, y, aq, asd)),
-            # every GEMV of the step in one launch; the K=128 activation has one consumer
-            # and is quantized inside the launch
-            ("q8_gemv_shared_multi_plus_f32", lambda: q8.q8_gemv_shared_multi_plus_f32(
-                [S[n] for n in DEC_GROUP], aq, asd, S["W128"], x128.view(-1), [outs[n] for n in DEC_GROUP],
-                outs["W128"])),
+            # the producer and every GEMV of the step in one launch; the K=128 activation has
+            # one consumer and is quantized inside the launch
+            ("rmsnorm_quant_gemv_shared_multi_plus_f32", lambda: q8.rmsnorm_quant_gemv_shared_multi_plus_f32(
+                x, w, EPS, [S[n] for n in DEC_GROUP], S["W128"], x128.view(-1), y, aq, asd,
+                [outs[n] for n in DEC_GROUP], outs["W128"])),
         ]
 
-    def standalone(c):  # the same GEMVs as separate launches, for comparison
+    def standalone(c):  # the same work as separate launches, for comparison
         S = sets[c % ncopy]
         return {
+            # the step as two launches: the producer, then both GEMVs in one launch
+            "rmsnorm_quant_row": (lambda: q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_ROW, y, aq, asd), rms_bytes(1, H)),
+            "q8_gemv_shared_multi_plus_f32": (lambda: q8.q8_gemv_shared_multi_plus_f32(
+                [S[n] for n in DEC_GROUP], aq, asd, S["W128"], x128.view(-1), [outs[n] for n in DEC_GROUP],
+                outs["W128"]), decode_pair_bytes()),
             # the step's GEMVs as two launches
             "q8_gemv_shared_multi_x6": (lambda: q8.q8_gemv_shared_multi(
                 [S[n] for n in DEC_GROUP], aq, asd, [outs[n] for n in DEC_GROUP]), decode_grouped_bytes()),
@@ -320,7 +328,7 @@ def bench_decode(D, steps, warmup, log_reps):
     del gw
     return {"ms_per_step": ms / steps, "step_bytes": step_bytes, "value_GBps": step_bytes * steps / (ms * 1e-3) / 1e9,
             "copies": ncopy, "components": comp, "launches_per_step": sum(counted.values()),
-            "launches_per_step_predicted": 2,
+            "launches_per_step_predicted": 1,
             "warm": {"ms_per_step": warm_ms / steps, "GBps": step_bytes * steps / (warm_ms * 1e-3) / 1e9,
                      "note": "one weight copy, resident in the Infinity Cache; not the headline"},
             "launch_counts_per_step": counted}
@@ -642,7 +650,7 @@ def main():
             log(f"[{name}] running")
             per[name] = fn(D, args.reps)
             torch.cuda.empty_cache()
-    dom_name = "q8_gemv_shared_multi_plus_f32"
+    dom_name = "rmsnorm_quant_gemv_shared_multi_plus_f32"
     dom = dec["components"][dom_name]
     # average launch duration: HIP events around a batch of back-to-back launches on the
     # launch stream (weights rotate over cold copies); per-launch event pairs are in components
@@ -660,9 +668,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": dec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": "decode_h7168", "batch": 1, "hidden": 7168,
-                   "gemvs": "rmsnorm_quant ROW -> one launch (q8_gemv_shared_multi_plus_f32): the grouped GEMV "
-                            "over N=4096/512/512/4096/12288/96 (K=7168) and the N=4096 K=128 GEMV, whose f32 "
-                            "activation is quantized in the launch",
+                   "gemvs": "one launch (rmsnorm_quant_gemv_shared_multi_plus_f32): rmsnorm_quant ROW of the "
+                            "row, the grouped GEMV over N=4096/512/512/4096/12288/96 (K=7168) on it, and the "
+                            "N=4096 K=128 GEMV, whose f32 activation is quantized in the launch",
                    "launches_per_step": dec["launches_per_step"],
                    "launches_per_step_predicted": dec["launches_per_step_predicted"],
                    "launch_counts_per_step": dec["launch_counts_per_step"], "weight_copies": dec["copies"],

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define Q8PROJ_ABI_VERSION 2
+#define Q8PROJ_ABI_VERSION 3
 
 /* return codes */
 #define Q8_OK 0
@@ -119,7 +119,8 @@ const char* q8_strerror(int code);
 #define Q8_LAUNCH_Q4K_GEMM 8              /* q4k_gemm */
 #define Q8_LAUNCH_WEIGHTS_REPACK 9        /* q8_weights_repack */
 #define Q8_LAUNCH_GEMV_SHARED_MULTI_PLUS_F32 10  /* q8_gemv_shared_multi_plus_f32 (1 launch, or 2: see there) */
-#define Q8_LAUNCH_COUNTERS 11
+#define Q8_LAUNCH_RMSNORM_GEMV_STEP 11   /* rmsnorm_quant_gemv_shared_multi_plus_f32, one-launch form */
+#define Q8_LAUNCH_COUNTERS 12
 
 /* Copies the first min(n, Q8_LAUNCH_COUNTERS) counters, in the order of the
  * Q8_LAUNCH_* ids, into the host array counts. Returns Q8_LAUNCH_COUNTERS,
@@ -234,6 +235,30 @@ int q8_gemv_shared_multi_ex(int m, const q8_weights* const* W, const int8_t* a_q
  */
 int q8_gemv_shared_multi_plus_f32(int m, const q8_weights* const* W, const int8_t* a_qs, const uint32_t* a_sd,
                                   float* const* y, const q8_weights* Wx, const float* x, float* yx, void* stream);
+
+/*
+ * The decode step of one layer's projections in one launch: rmsnorm_quant of
+ * the single row x (width K = W[i]->k, ROW layout) and
+ * q8_gemv_shared_multi_plus_f32 of its consumers ([P2] s2-s3: the producer
+ * writes the q8_0 activation in the same pass as its f32 output, and the
+ * consumers read it; [P1] s3: at decode a launch costs more than its bytes).
+ * Inside the launch every workgroup of the grouped GEMV normalizes and
+ * quantizes the row into its own LDS and reads its activation from there, so
+ * no workgroup waits for another; x and w are read from HBM once per XCD.
+ *   x, w: device f32, K values each, 16-byte aligned. eps: as rmsnorm_quant.
+ *   y: device f32 [K] for the normalized row, or NULL for none.
+ *   a_qs, a_sd: device buffers (K bytes, K/32 words; 16- and 4-byte aligned)
+ *     that receive the row's q8_0 activation, as rmsnorm_quant writes it.
+ *   m, W, ys, Wx, x2, yx: as q8_gemv_shared_multi_plus_f32 (m, W, y, Wx, x, yx).
+ * Every output is bit-identical to rmsnorm_quant followed by
+ * q8_gemv_shared_multi_plus_f32. The one launch serves the pair launch's
+ * shapes (see there) with both parts non-empty; other shapes run those two
+ * calls back to back (and count under their names). Errors: those of the two
+ * calls, all checked before anything is launched; Q8_EINVAL for a NULL x or w.
+ */
+int rmsnorm_quant_gemv_shared_multi_plus_f32(const float* x, const float* w, float eps, float* y, int8_t* a_qs,
+                                             uint32_t* a_sd, int m, const q8_weights* const* W, float* const* ys,
+                                             const q8_weights* Wx, const float* x2, float* yx, void* stream);
 
 /*
  * The GEMV launch plan for `total_rows` rows of width K (host only):

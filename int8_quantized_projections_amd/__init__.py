@@ -26,5 +26,6 @@ from .q8lib import (  # noqa: F401
     q8_quantize,
     q8_weights_repack,
     rmsnorm_quant,
+    rmsnorm_quant_gemv_shared_multi_plus_f32,
     swiglu_quant,
 )

@@ -21,6 +21,7 @@
 //    W lanes. The order depends on K only, so 1, 2 or 4 rows per wave and the
 //    grouped launch give bit-identical outputs ([P1] s8 invariant).
 #include "q8_common.h"
+#include "rmsnorm_row.h"
 
 #include <type_traits>
 
@@ -238,6 +239,57 @@ __global__ __launch_bounds__(256) void k_gemv_pair(GemvArgs a1, const int8_t* __
         gemv_run<W, NBL, R, true, false>(a1, aq, asd, nullptr, K1, nb1, groups1,
                                          (int64_t)(blockIdx.x - wgs2) * kWavesPerWg + w,
                                          (int64_t)(gridDim.x - wgs2) * kWavesPerWg);
+}
+
+// The one-launch decode step: rmsnorm_quant of one row and the paired GEMVs of
+// its consumers ([P1] s3: at decode a launch costs more than its bytes; [P2]
+// s2: the producer's q8_0 output is what the consumers read). Workgroups
+// [0, wgs2) run the f32-activation GEMV; every other workgroup first runs the
+// producer itself, the same code with the same 16-wave layout as the
+// standalone rmsnorm_quant of one row (so the same bits), into its own LDS,
+// then runs the grouped GEMV from that copy. The first grouped workgroup also
+// writes y and the q8_0 activation to memory.
+//
+// Per workgroup that is 56 KB of L2 reads (x and w at K=7168; HBM serves them
+// once per XCD) and a few hundred instructions, with no dependency between
+// workgroups. Measured alternatives, per decode step (two launches: 33.9 us;
+// this form: 32.8 us):
+//  - one producer workgroup that the others wait for (a flag in memory, an
+//    agent-scope release and acquire, one poller per workgroup): 35.5 us, as
+//    every load issued behind the first rows' weight loads, the producer's and
+//    the polls alike, waits for that queue;
+//  - this form with the first weight loads issued before the producer's
+//    arithmetic: 32.9 us with the x and w loads after them, 35.7 us with the
+//    x and w loads first (then the registers spill).
+constexpr int kStepWaves = 16;    // waves per workgroup of the decode step
+constexpr int kMaxStepK = 8192;   // the grouped part's K: one chunk of 64 lanes x 4 blocks
+
+template <int NV, int NBL, int R, int W2>
+__global__ __launch_bounds__(kStepWaves * 64) void k_decode_step(
+    const float* __restrict__ xn, const float* __restrict__ wn, float eps, float* __restrict__ yn,
+    int8_t* __restrict__ aq_out, uint32_t* __restrict__ asd_out, GemvArgs a1, int K1, int nb1, int64_t groups1,
+    GemvArgs a2, const float* __restrict__ x2, int K2, int nb2, int64_t groups2, int wgs2) {
+    __shared__ __attribute__((aligned(16))) int8_t act_q[kMaxStepK];
+    __shared__ uint32_t act_sd[kMaxStepK / kQK];
+    const int w = threadIdx.x >> 6;
+    const int b = (int)blockIdx.x;
+    if (b < wgs2) {
+        gemv_run<W2, 1, 1, false, true>(a2, nullptr, nullptr, x2, K2, nb2, groups2, (int64_t)b * kStepWaves + w,
+                                        (int64_t)wgs2 * kStepWaves);
+        return;
+    }
+    const bool writer = b == wgs2;
+    rmsnorm_rows<kDstRow, NV, kStepWaves, kStepWaves>(xn, wn, eps, writer ? yn : nullptr, 1, 1, K1, nb1, act_q,
+                                                      act_sd, 0);
+    __syncthreads();
+    if (writer) {
+        for (int i = (int)threadIdx.x; i < K1 / 16; i += kStepWaves * 64)
+            reinterpret_cast<uint4*>(aq_out)[i] = reinterpret_cast<const uint4*>(act_q)[i];
+        for (int i = (int)threadIdx.x; i < nb1; i += kStepWaves * 64) asd_out[i] = act_sd[i];
+    }
+    gemv_run<64, NBL, R, true, false>(a1, act_q, act_sd, nullptr, K1, nb1, groups1,
+                                      (int64_t)(b - wgs2) * kStepWaves + w,
+                                      (int64_t)((int)gridDim.x - wgs2) * kStepWaves);
 }
 
 struct Plan {
@@ -482,6 +534,46 @@ void launch_pair(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const int8
     }
 }
 
+// The decode step's producer holds the row in NV float4 per lane over 16
+// waves, as rmsnorm_quant does for one row: 1 for K <= 4096, 2 for K <= 8192.
+int step_nv(int K) {
+    const int need = (int)q8h::ceil_div(K / 4, (int64_t)kStepWaves * kWave);
+    return need <= 1 ? 1 : need <= 2 ? 2 : 0;
+}
+
+// The one-launch step serves the pair kernel's shapes with one row per wave
+// (the grouped part's plan at one K chunk, K <= 8192) and both parts non-empty.
+bool step_supported(const GemvJob& j1, const GemvJob& j2) {
+    return !j1.empty && !j2.empty && pair_supported(j1.p, j2.p) && j1.p.rows == 1 && j1.K <= kMaxStepK &&
+           step_nv(j1.K) > 0 && (step_nv(j1.K) == 1) == (j1.p.nbl == 2);
+}
+
+template <int NV, int NBL, int W2>
+void launch_step3(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const float* x, const float* w, float eps,
+                  float* y, int8_t* a_qs, uint32_t* a_sd, const float* x2) {
+    // the f32 part keeps its wave count; the grouped part takes the resident
+    // 16-wave slots that the f32 part leaves (at least one workgroup)
+    const int64_t waves2 = j2.p.groups < kMaxWaves ? j2.p.groups : kMaxWaves;
+    const int wgs2 = (int)q8h::ceil_div(waves2, (int64_t)kStepWaves);
+    const int64_t cap = kMaxWaves / kStepWaves - wgs2;
+    const int64_t want = q8h::ceil_div(j1.p.groups, (int64_t)kStepWaves);
+    const int64_t wgs1 = want < cap ? want : (cap > 0 ? cap : 1);
+    const dim3 grid((unsigned)(wgs2 + wgs1));
+    hipLaunchKernelGGL((k_decode_step<NV, NBL, 1, W2>), grid, dim3(kStepWaves * 64), 0, s, x, w, eps, y, a_qs, a_sd,
+                       j1.a, j1.K, j1.nb, j1.p.groups, j2.a, x2, j2.K, j2.nb, j2.p.groups, wgs2);
+}
+
+template <int NV, int NBL>
+void launch_step2(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const float* x, const float* w, float eps,
+                  float* y, int8_t* a_qs, uint32_t* a_sd, const float* x2) {
+    if (j2.p.lanes == 4)
+        launch_step3<NV, NBL, 4>(j1, j2, s, x, w, eps, y, a_qs, a_sd, x2);
+    else if (j2.p.lanes == 8)
+        launch_step3<NV, NBL, 8>(j1, j2, s, x, w, eps, y, a_qs, a_sd, x2);
+    else
+        launch_step3<NV, NBL, 16>(j1, j2, s, x, w, eps, y, a_qs, a_sd, x2);
+}
+
 }  // namespace
 
 extern "C" {
@@ -548,6 +640,29 @@ int q8_gemv_shared_multi_plus_f32(int m, const q8_weights* const* W, const int8_
         if ((rc = q8h::launch_status(ctr))) return rc;
     }
     return Q8_OK;
+}
+
+int rmsnorm_quant_gemv_shared_multi_plus_f32(const float* x, const float* w, float eps, float* y, int8_t* a_qs,
+                                             uint32_t* a_sd, int m, const q8_weights* const* W, float* const* ys,
+                                             const q8_weights* Wx, const float* x2, float* yx, void* stream) {
+    GemvJob j1, j2;
+    int rc = prepare_multi(m, W, a_qs, a_sd, ys, 0, j1);
+    if (rc) return rc;
+    if ((rc = prepare_f32(Wx, x2, yx, j2))) return rc;
+    if (x == nullptr || w == nullptr) return Q8_EINVAL;
+    if (!q8h::aligned(x, 16) || !q8h::aligned(w, 16) || !q8h::aligned(y, 16)) return Q8_EALIGN;
+    const int64_t K = W[0]->k;
+    const hipStream_t s = (hipStream_t)stream;
+    if (step_supported(j1, j2)) {
+        if (j1.p.nbl == 2)
+            launch_step2<1, 2>(j1, j2, s, x, w, eps, y, a_qs, a_sd, x2);
+        else
+            launch_step2<2, 4>(j1, j2, s, x, w, eps, y, a_qs, a_sd, x2);
+        return q8h::launch_status(Q8_LAUNCH_RMSNORM_GEMV_STEP);
+    }
+    // other shapes: the producer, then the pair (or its two kernels)
+    if ((rc = rmsnorm_quant(x, w, eps, y, 1, K, Q8_LAYOUT_ROW, a_qs, a_sd, stream))) return rc;
+    return q8_gemv_shared_multi_plus_f32(m, W, a_qs, a_sd, ys, Wx, x2, yx, stream);
 }
 
 int q8_gemv(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, float* y, void* stream) {

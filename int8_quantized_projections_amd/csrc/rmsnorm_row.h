@@ -1,0 +1,187 @@
+// RMSNorm + quantize device code shared by rmsnorm_quant (producers.hip) and
+// the one-launch decode step (gemv.hip), so the two write the same bits.
+//
+// Sources: [P2] "r51 producer-fused A-quantize" s2-s3 (the fused producer, the
+// 64-token plane and its zero tail), [P3] "r5-r6 rewrite spec" point 7
+// (tree-reduced amax, packed stores).
+#pragma once
+
+#include "q8_common.h"
+
+namespace q8 {
+namespace {
+
+enum Dst : int { kDstNone = 0, kDstRow = 1, kDstPlane = 2 };
+
+// Streaming accesses: the non-temporal bit, so the line does not displace
+// others from L2 and the MALL. Measured per stream, not applied wholesale:
+// - every f32 output y and the PLANE64 tile stores: 5.1 -> 5.4 TB/s on the
+//   3325x18944 swiglu_quant with the plane, 3.2 -> 3.6 on the 3325x18944
+//   rmsnorm_quant, and never slower;
+// - the gate and up inputs of swiglu_quant (row layout 5.3 -> 6.1 TB/s);
+// - not the single input of q8_quantize or rmsnorm_quant: there they measured
+//   slower (rmsnorm_quant 3325x3584, 21 -> 25 us), as a row that the previous
+//   kernel just wrote is often still in the MALL;
+// - not the RMSNorm weight row, which every row reads.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(float* p, const float4& v) {
+    const f32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ void store_stream(void* p, const uint4& v) {
+    const u32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
+
+// Write this lane's 4 quantized values (and, from the group's first lane,
+// the block's scale word) for element e..e+3 of chunk c of row t.
+template <int D>
+__device__ __forceinline__ void store_quant(const Quant8& r, int64_t t, int c, int e, int K, int nb, int8_t* qs,
+                                            uint32_t* sd) {
+    if constexpr (D == kDstRow) {
+        *reinterpret_cast<uint32_t*>(qs + t * K + (int64_t)c * kQK + e) = r.qs4;
+        if (e == 0) sd[t * nb + c] = r.sd;
+    } else if constexpr (D == kDstPlane) {
+        *reinterpret_cast<uint32_t*>(qs + plane_qs_off(t, c, e, nb)) = r.qs4;
+        if (e == 0) sd[plane_sd_idx(t, c, nb)] = r.sd;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm + quantize of the rows of logical workgroup `wg` (WAVES / WPR rows,
+// WPR waves per row). The row stays in registers (NV float4 per lane,
+// K <= 256*WPR*NV) between the sum of squares and the output, so x is read
+// once, and w is loaded in the same wave of loads. Lane i of the row
+// (i = 64*(wave % WPR) + lane) holds float4 index i + 64*WPR*k; 8 consecutive
+// lanes hold one 32-value block. The sum of squares, and so every output bit,
+// depends on K, WPR and NV only.
+// NV == 0: rows wider than the register budget; x is read twice (the second
+// read hits L2), with the same per-lane order of the sum of squares.
+// Every wave of the workgroup must call it (WPR > 1 combines the waves'
+// partial sums through LDS behind a barrier). qs and sd may point to LDS.
+// ---------------------------------------------------------------------------
+template <int D, int NV, int WPR, int WAVES>
+__device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const float* __restrict__ w, float eps,
+                                             float* __restrict__ y, int64_t rows, int64_t tpad, int K, int nb,
+                                             int8_t* __restrict__ qs, uint32_t* __restrict__ sd, int64_t wg) {
+    static_assert(WAVES % WPR == 0, "whole rows per workgroup");
+    constexpr int kRowsPerWg = WAVES / WPR;
+    constexpr int kStride = kWave * WPR;  // float4 stride between a lane's elements
+    __shared__ float part[WAVES];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = wg * kRowsPerWg + wave / WPR;
+    const int li = (wave % WPR) * kWave + lane;  // lane index inside the row
+    const bool live = t < rows;
+    const bool inrow = t < tpad;  // uniform per wave
+    const int n4 = K >> 2;
+    const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x + (live ? t : 0) * K);
+    const float4* __restrict__ w4 = reinterpret_cast<const float4*>(w);
+    // y == NULL: the quantized output only, no f32 row is written
+    float4* __restrict__ y4 = y != nullptr ? reinterpret_cast<float4*>(y + (live ? t : 0) * K) : nullptr;
+
+    auto row_sum = [&](float ss) {
+        ss = wave_sum(ss);
+        if constexpr (WPR > 1) {
+            if (lane == 0) part[wave] = ss;
+            __syncthreads();
+            const int w0 = (wave / WPR) * WPR;
+            ss = part[w0];
+#pragma unroll
+            for (int i = 1; i < WPR; ++i) ss += part[w0 + i];
+        }
+        return ss;
+    };
+
+    if constexpr (NV > 0) {
+        float4 v[NV], wv[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int idx = li + kStride * k;
+            const int ic = idx < n4 ? idx : n4 - 1;
+            v[k] = x4[ic];
+            wv[k] = w4[ic];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep every x and w load ahead of the math
+        // masks applied only after every load is in flight
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            if (!live || li + kStride * k >= n4) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            ss = fmaf(v[k].x, v[k].x, ss);
+            ss = fmaf(v[k].y, v[k].y, ss);
+            ss = fmaf(v[k].z, v[k].z, ss);
+            ss = fmaf(v[k].w, v[k].w, ss);
+        }
+        ss = row_sum(ss);
+        if (!inrow) return;
+        // [P2] s3.2: scale = rsqrt(ss/d + eps), y = x * scale * w.
+        const float scale = rsqrtf(ss / (float)K + eps);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int idx = li + kStride * k;
+            float4 o;
+            o.x = v[k].x * scale * wv[k].x;
+            o.y = v[k].y * scale * wv[k].y;
+            o.z = v[k].z * scale * wv[k].z;
+            o.w = v[k].w * scale * wv[k].w;
+            if (y4 != nullptr && live && idx < n4) store_stream(reinterpret_cast<float*>(y4 + idx), o);
+            v[k] = o;  // zero for padded rows and past K
+        }
+        if constexpr (D != kDstNone) {
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int c = (li + kStride * k) >> 3;
+                if (c < nb) {
+                    const Quant8 r = quantize_block8(v[k]);
+                    store_quant<D>(r, t, c, (lane & 7) * 4, K, nb, qs, sd);
+                }
+            }
+        }
+    } else {
+        float ss = 0.0f;
+        if (live) {
+            for (int idx = li; idx < n4; idx += kStride) {
+                const float4 a = x4[idx];
+                ss = fmaf(a.x, a.x, ss);
+                ss = fmaf(a.y, a.y, ss);
+                ss = fmaf(a.z, a.z, ss);
+                ss = fmaf(a.w, a.w, ss);
+            }
+        }
+        ss = row_sum(ss);
+        if (!inrow) return;
+        const float scale = rsqrtf(ss / (float)K + eps);
+        const int steps = (n4 + kStride - 1) / kStride;
+        for (int k = 0; k < steps; ++k) {
+            const int idx = li + kStride * k;
+            const int ic = idx < n4 ? idx : n4 - 1;
+            const float4 a = x4[ic];
+            const float4 wq = w4[ic];
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (live && idx < n4) {
+                o.x = a.x * scale * wq.x;
+                o.y = a.y * scale * wq.y;
+                o.z = a.z * scale * wq.z;
+                o.w = a.w * scale * wq.w;
+                if (y4 != nullptr) store_stream(reinterpret_cast<float*>(y4 + idx), o);
+            }
+            if constexpr (D != kDstNone) {
+                const int c = idx >> 3;
+                if (c < nb) {
+                    const Quant8 r = quantize_block8(o);
+                    store_quant<D>(r, t, c, (lane & 7) * 4, K, nb, qs, sd);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+}  // namespace q8

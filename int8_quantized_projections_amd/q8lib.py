@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
                                      ci),
             "q8_weights_repack": ([vp, i64, i64, vp, vp, vp], ci),
             "q8_gemv_shared_multi_plus_f32": ([ci, ctypes.POINTER(wp), vp, vp, ctypes.POINTER(vp), wp, vp, vp, vp], ci),
+            "rmsnorm_quant_gemv_shared_multi_plus_f32": ([vp, vp, ctypes.c_float, vp, vp, vp, ci, ctypes.POINTER(wp),
+                                                          ctypes.POINTER(vp), wp, vp, vp, vp], ci),
             "q8_launch_counts": ([ctypes.POINTER(i64), ci], ci),
             "q8_launch_counts_reset": ([], None),
             "q8_launch_counter_name": ([ci], ctypes.c_char_p),
@@ -295,6 +297,34 @@ def q8_gemv_shared_multi_plus_f32(Ws: list[Q8Weights], a_qs: torch.Tensor, a_sd:
     _check(lib().q8_gemv_shared_multi_plus_f32(m, wps, _ptr(a_qs), _ptr(a_sd), yps, ctypes.byref(wx), _ptr(x),
                                                _ptr(yx), _stream(a_qs.device)), "q8_gemv_shared_multi_plus_f32")
     return ys, yx
+
+
+def rmsnorm_quant_gemv_shared_multi_plus_f32(x: torch.Tensor, w: torch.Tensor, eps: float, Ws: list[Q8Weights],
+                                             Wx: Q8Weights, x2: torch.Tensor, y=None, a_qs=None, a_sd=None, ys=None,
+                                             yx=None, f32: bool = True):
+    """rmsnorm_quant of the row x (ROW layout) and q8_gemv_shared_multi_plus_f32 of its consumers, in one
+    launch where the shapes allow. f32=False passes y = NULL. Returns (y, a_qs, a_sd, ys, yx)."""
+    rows, k = _rows_k(x)
+    if rows != 1:
+        raise ValueError("the decode step normalizes one row")
+    if y is None and f32:
+        y = torch.empty_like(x)
+    if a_qs is None:
+        a_qs, a_sd = alloc_act(1, k, LAYOUT_ROW, x.device)
+    m = len(Ws)
+    if ys is None:
+        ys = [torch.empty(W.n, dtype=torch.float32, device=x.device) for W in Ws]
+    if yx is None:
+        yx = torch.empty(Wx.n, dtype=torch.float32, device=x.device)
+    structs = [W.struct() for W in Ws]
+    wps = (ctypes.POINTER(_Weights) * m)(*[ctypes.pointer(st) for st in structs])
+    yps = (ctypes.c_void_p * m)(*[_ptr(t) for t in ys])
+    wx = Wx.struct()
+    _check(lib().rmsnorm_quant_gemv_shared_multi_plus_f32(_ptr(x), _ptr(w), eps, _ptr(y), _ptr(a_qs), _ptr(a_sd), m,
+                                                          wps, yps, ctypes.byref(wx), _ptr(x2), _ptr(yx),
+                                                          _stream(x.device)),
+           "rmsnorm_quant_gemv_shared_multi_plus_f32")
+    return y, a_qs, a_sd, ys, yx
 
 
 def gemv_plan(total_rows: int, k: int, rows_per_wave: int = 0) -> dict:

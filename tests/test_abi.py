@@ -41,7 +41,7 @@ def test_exports_every_declared_function(L):
     assert len(names) >= 12
     for n in names:
         assert hasattr(L, n), f"{n} declared in q8proj.h but not exported"
-    assert L.q8_abi_version() == 2
+    assert L.q8_abi_version() == 3
     assert L.q8_strerror(-3).decode().startswith("pointer not aligned")
 
 
@@ -254,4 +254,37 @@ def test_gemv_pair_rejects_before_launch(L):
     assert fn(2, two, f, f, (ctypes.c_void_p * 2)(f, f), ctypes.byref(W), f, f, None) == Q8_ESHAPE
     # both parts empty: valid, nothing launched
     assert fn(1, w0, f, f, ys, ctypes.byref(W0), f, f, None) == Q8_OK
+    assert all(v == 0 for v in q8lib.launch_counts().values())
+
+
+def test_decode_step_rejects_before_launch(L):
+    """rmsnorm_quant_gemv_shared_multi_plus_f32 checks the producer's and both GEMVs' arguments
+    before launching anything, on the one-launch path and the fallback alike."""
+    f = FAKE
+    W = q8lib._Weights(8, 4096, ctypes.c_void_p(f), ctypes.c_void_p(f))
+    Wx = q8lib._Weights(64, 128, ctypes.c_void_p(f), ctypes.c_void_p(f))
+    Wbig = q8lib._Weights(8, 8224, ctypes.c_void_p(f), ctypes.c_void_p(f))
+    W96 = q8lib._Weights(8, 96, ctypes.c_void_p(f), ctypes.c_void_p(f))
+    wps = (ctypes.POINTER(q8lib._Weights) * 1)(ctypes.pointer(W))
+    ys = (ctypes.c_void_p * 1)(f)
+    fn = L.rmsnorm_quant_gemv_shared_multi_plus_f32
+    wx = ctypes.byref(Wx)
+
+    def call(x=f, w=f, y=f, aq=f, asd=f, m=1, W=wps, Y=ys, WX=wx, x2=f, yx=f):
+        return fn(x, w, 1e-6, y, aq, asd, m, W, Y, WX, x2, yx, None)
+
+    L.q8_launch_counts_reset()
+    assert call(x=None) == Q8_EINVAL
+    assert call(w=None) == Q8_EINVAL
+    assert call(x=f + 4) == Q8_EALIGN
+    assert call(w=f + 8) == Q8_EALIGN
+    assert call(y=f + 4) == Q8_EALIGN
+    assert call(aq=None) == Q8_EINVAL                 # the activation buffers are required
+    assert call(aq=f + 4) == Q8_EALIGN
+    assert call(m=0) == Q8_EINVAL
+    assert call(WX=None) == Q8_EINVAL
+    assert call(WX=ctypes.byref(Wbig)) == Q8_ESHAPE   # f32 part K > 8192
+    assert call(x2=f + 4) == Q8_EALIGN
+    two = (ctypes.POINTER(q8lib._Weights) * 2)(ctypes.pointer(W), ctypes.pointer(W96))
+    assert call(m=2, W=two, Y=(ctypes.c_void_p * 2)(f, f)) == Q8_ESHAPE  # grouped members share K
     assert all(v == 0 for v in q8lib.launch_counts().values())

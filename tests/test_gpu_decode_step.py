@@ -1,0 +1,161 @@
+"""The one-launch decode step, rmsnorm_quant_gemv_shared_multi_plus_f32: rmsnorm_quant of one
+row and the grouped + f32 GEMVs of its consumers in one launch, each grouped workgroup running
+the producer into its own LDS ([P2] s2: the producer writes the quantized activation its
+consumers read; [P1] s3: a launch at decode costs more than its bytes).
+
+Bars:
+- every output (y, the q8_0 activation, each grouped output, the f32 part) is bit-identical to
+  rmsnorm_quant followed by q8_gemv_shared_multi_plus_f32, each of which the other GPU tests
+  pin to the oracle; y is also checked against the oracle's f64 RMSNorm (1e-5) and the
+  activation against the oracle's quantize of that reference;
+- consecutive calls on different rows each give their own row's results;
+- the one-launch form counts one launch; other shapes fall back to the two calls;
+- graph replays reproduce the eager results, with eager calls and synchronizations between.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _gpu import assert_rel, ensure_built, poisoned, to_np, up, weights
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+ensure_built()
+from int8_quantized_projections_amd import q8lib  # noqa: E402
+
+ROW = q8lib.LAYOUT_ROW
+EPS = 1e-6
+STEP = "rmsnorm_quant_gemv_shared_multi_plus_f32"
+
+# (grouped N list, K, f32-part N, its K, one launch?)
+CASES = [
+    ([4096, 512, 512, 4096, 12288, 96], 7168, 4096, 128, True),  # the decode projection set
+    ([300, 200], 3584, 100, 256, True),
+    ([129], 2080, 33, 512, True),
+    ([5, 0, 70], 4096, 7, 96, True),       # fewer rows than waves: most waves never wait
+    ([1000, 24], 8192, 64, 128, True),
+    ([77], 4128, 16, 128, True),
+    ([64], 1024, 64, 128, False),          # K too narrow for the pair kernel: the two calls
+    ([300], 3584, 0, 128, False),          # empty f32 part
+    ([0, 0], 3584, 40, 128, False),        # empty grouped part
+]
+
+
+def _weights_or_empty(n, K, stream):
+    W = weights(synth.normal((max(n, 1), K), stream=stream, std=0.02))[0]
+    return W if n else W.rows(0, 0)
+
+
+def _inputs(Ns, K, Nx, Kx, base):
+    Ws = [_weights_or_empty(n, K, base + 7 * i) for i, n in enumerate(Ns)]
+    Wx = _weights_or_empty(Nx, Kx, base + 50)
+    w = synth.normal((K,), stream=base + 51, mean=1.0, std=0.1)
+    return Ws, Wx, w
+
+
+def _reference(x, w, Ws, Wx, x2):
+    """rmsnorm_quant, then q8_gemv_shared_multi_plus_f32: the two-call form."""
+    y, aq, asd = q8lib.rmsnorm_quant(x, w, EPS, ROW)
+    ys, yx = q8lib.q8_gemv_shared_multi_plus_f32(Ws, aq, asd, Wx, x2)
+    return y, aq, asd, ys, yx
+
+
+class Outs:
+    def __init__(self, K, Ws, Wx):
+        self.y = poisoned(K, torch.float32, 0xFF).view(1, K)
+        nq, ns = q8lib.act_bytes(1, K, ROW)
+        self.aq, self.asd = poisoned(nq, torch.int8), poisoned(ns // 4, torch.int32)
+        self.ys = [poisoned(max(W.n, 1), torch.float32, 0xFF)[: W.n] for W in Ws]
+        self.yx = poisoned(max(Wx.n, 1), torch.float32, 0xFF)[: Wx.n]
+
+    def step(self, x, w, Ws, Wx, x2):
+        q8lib.rmsnorm_quant_gemv_shared_multi_plus_f32(x, w, EPS, Ws, Wx, x2, self.y, self.aq, self.asd, self.ys,
+                                                       self.yx)
+
+    def all(self):
+        return [self.y, self.aq, self.asd, *self.ys, self.yx]
+
+
+def _assert_same(got, ref, what):
+    names = ["y", "a_qs", "a_sd"] + [f"y[{i}]" for i in range(len(got) - 4)] + ["yx"]
+    for g, r, n in zip(got, ref, names):
+        assert torch.equal(g.reshape(-1).view(torch.int32 if g.dtype == torch.float32 else g.dtype),
+                           r.reshape(-1).view(torch.int32 if r.dtype == torch.float32 else r.dtype)), \
+            f"{what}: {n} differs from the two-call form"
+
+
+@pytest.mark.parametrize("Ns,K,Nx,Kx,one", CASES)
+def test_step_bit_identical_to_two_calls(Ns, K, Nx, Kx, one):
+    Ws, Wx, wh = _inputs(Ns, K, Nx, Kx, 8100 + K + Kx)
+    w = up(wh)
+    o = Outs(K, Ws, Wx)
+    # three different rows in a row: each call must read its own row's activation
+    for r in range(3):
+        xh = synth.normal((1, K), stream=8200 + 3 * K + r)
+        x, x2 = up(xh), up(synth.normal((Kx,), stream=8300 + Kx + r))
+        ref = _reference(x, w, Ws, Wx, x2)
+        torch.cuda.synchronize()
+        q8lib.launch_counts_reset()
+        o.step(x, w, Ws, Wx, x2)
+        torch.cuda.synchronize()
+        c = {k: v for k, v in q8lib.launch_counts().items() if v}
+        if one:
+            assert c == {STEP: 1}, c
+        else:
+            assert c.get(STEP, 0) == 0 and c["rmsnorm_quant"] == 1, c
+        _assert_same([o.y, o.aq, o.asd, *o.ys, o.yx], [ref[0], ref[1], ref[2], *ref[3], ref[4]],
+                     f"{Ns}x{K} + {Nx}x{Kx}, row {r}")
+        if r == 0:  # the producer's output against the oracle
+            y_ref = oracle.rmsnorm_f64(xh, wh, EPS)
+            assert_rel(to_np(o.y), y_ref, 1e-5, f"rmsnorm 1x{K}")
+            q = to_np(o.aq).reshape(1, K)
+            d16, s = oracle.unpack_sd(to_np(o.asd).view(np.uint32).reshape(1, K // 32))
+            qo, do, _ = oracle.quantize(y_ref.astype(np.float32))
+            assert np.abs(q.astype(int) - qo.astype(int)).max() <= 1
+            assert np.abs(d16.astype(int) - do.astype(int)).max() <= 1
+            assert np.array_equal(s.astype(np.int64), q.reshape(1, -1, 32).astype(np.int64).sum(axis=2))
+
+
+def test_step_without_f32_output():
+    """y = NULL writes only the quantized activation and the GEMV outputs, with the same bits."""
+    Ns, K, Nx, Kx = [4096, 512], 7168, 512, 128
+    Ws, Wx, wh = _inputs(Ns, K, Nx, Kx, 8400)
+    w = up(wh)
+    x, x2 = up(synth.normal((1, K), stream=8401)), up(synth.normal((Kx,), stream=8402))
+    a, b = Outs(K, Ws, Wx), Outs(K, Ws, Wx)
+    a.step(x, w, Ws, Wx, x2)
+    q8lib.rmsnorm_quant_gemv_shared_multi_plus_f32(x, w, EPS, Ws, Wx, x2, None, b.aq, b.asd, b.ys, b.yx, f32=False)
+    torch.cuda.synchronize()
+    assert torch.all(b.y.view(torch.int32) == -1), "y written although NULL was passed"
+    for g, r in zip(b.all()[1:], a.all()[1:]):
+        assert torch.equal(g, r)
+
+
+def test_step_graph_replays_match_eager():
+    Ns, K, Nx, Kx = [4096, 512, 512, 4096, 12288, 96], 7168, 4096, 128
+    Ws, Wx, wh = _inputs(Ns, K, Nx, Kx, 8500)
+    w = up(wh)
+    x, x2 = up(synth.normal((1, K), stream=8501)), up(synth.normal((Kx,), stream=8502))
+    xo, x2o = up(synth.normal((1, K), stream=8503)), up(synth.normal((Kx,), stream=8504))
+    ref = _reference(x, w, Ws, Wx, x2)
+    ref = [ref[0], ref[1], ref[2], *ref[3], ref[4]]
+    g_out, e_out = Outs(K, Ws, Wx), Outs(K, Ws, Wx)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    q8lib.launch_counts_reset()
+    with torch.cuda.graph(g):
+        g_out.step(x, w, Ws, Wx, x2)
+    assert {k: v for k, v in q8lib.launch_counts().items() if v} == {STEP: 1}
+    for i in range(3):
+        e_out.step(xo, w, Ws, Wx, x2o)  # eager work on other inputs between replays
+        torch.cuda.synchronize()
+        for t in g_out.all():
+            t.view(torch.uint8).fill_(0xFF)
+        g.replay()
+        torch.cuda.synchronize()
+        _assert_same(g_out.all(), ref, f"replay {i}")
+    assert not torch.equal(e_out.ys[0], ref[3])

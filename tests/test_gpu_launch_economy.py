@@ -11,7 +11,8 @@ anything runs, and the measured counters must equal it exactly:
   consumers and q8_gemv_f32 for the K=128 consumer: 3;
 - the paired layer is rmsnorm_quant and q8_gemv_shared_multi_plus_f32, both
   GEMVs in one launch: 2;
-- the savings are therefore exactly 3 and 4 launches per layer, and all three
+- the one-launch layer is rmsnorm_quant_gemv_shared_multi_plus_f32: 1;
+- the savings are therefore exactly 3, 4 and 5 launches per layer, and all four
   forms give identical outputs.
 Launches captured into a graph count once, at capture; replays count nothing
 and reproduce the eager results bit for bit, with eager work and
@@ -75,6 +76,11 @@ def paired_layer(ws, x, w, x128, B):
                                         [B.out[n] for n in GROUP], B.out["W128"])
 
 
+def step_layer(ws, x, w, x128, B):
+    q8lib.rmsnorm_quant_gemv_shared_multi_plus_f32(x, w, EPS, [ws[n] for n in GROUP], ws["W128"], x128, B.y, B.aq,
+                                                   B.asd, [B.out[n] for n in GROUP], B.out["W128"])
+
+
 def unfused_layer(ws, x, w, x128, B):
     q8lib.rmsnorm_quant(x, w, EPS, ROW, B.y, B.aq, B.asd)
     q8lib.q8_gemv_shared_multi([ws[n] for n in GROUP[:4]], B.aq, B.asd, [B.out[n] for n in GROUP[:4]])
@@ -86,15 +92,17 @@ def unfused_layer(ws, x, w, x128, B):
 
 FUSED = {"rmsnorm_quant": 1, "q8_gemv_shared_multi": 1, "q8_gemv_f32": 1}
 PAIRED = {"rmsnorm_quant": 1, "q8_gemv_shared_multi_plus_f32": 1}
+STEP = {"rmsnorm_quant_gemv_shared_multi_plus_f32": 1}
 UNFUSED = {"rmsnorm_quant": 1, "q8_gemv_shared_multi": 1, "q8_gemv": 3, "q8_quantize": 1}
 
 
 def test_decode_launch_counts_match_model_arithmetic(decode):
     ws, x, w, x128 = decode
-    Bf, Bp, Bu = Buffers(ws), Buffers(ws), Buffers(ws)
+    Bf, Bp, Bs, Bu = Buffers(ws), Buffers(ws), Buffers(ws), Buffers(ws)
     torch.cuda.synchronize()
     measured = {}
-    for name, layer, B in (("fused", fused_layer, Bf), ("paired", paired_layer, Bp), ("unfused", unfused_layer, Bu)):
+    for name, layer, B in (("fused", fused_layer, Bf), ("paired", paired_layer, Bp), ("step", step_layer, Bs),
+                           ("unfused", unfused_layer, Bu)):
         q8lib.launch_counts_reset()
         for _ in range(LAYERS):
             layer(ws, x, w, x128, B)
@@ -102,14 +110,17 @@ def test_decode_launch_counts_match_model_arithmetic(decode):
     torch.cuda.synchronize()
     assert measured["fused"] == {k: LAYERS * v for k, v in FUSED.items()}
     assert measured["paired"] == {k: LAYERS * v for k, v in PAIRED.items()}
+    assert measured["step"] == {k: LAYERS * v for k, v in STEP.items()}
     assert measured["unfused"] == {k: LAYERS * v for k, v in UNFUSED.items()}
-    # the predicted savings, as counts: 3 and 4 launches per layer
+    # the predicted savings, as counts: 3, 4 and 5 launches per layer
     total = {k: sum(v.values()) for k, v in measured.items()}
     assert total["unfused"] - total["fused"] == 3 * LAYERS
     assert total["unfused"] - total["paired"] == 4 * LAYERS
-    for a, b, c, n in zip(Bf.outputs(), Bp.outputs(), Bu.outputs(), GROUP + ["W128"]):
+    assert total["unfused"] - total["step"] == 5 * LAYERS
+    for a, b, c, d, n in zip(Bf.outputs(), Bp.outputs(), Bs.outputs(), Bu.outputs(), GROUP + ["W128"]):
         assert not torch.isnan(a).any(), n
-        assert torch.equal(a, b) and torch.equal(a, c), f"{n}: the layer forms differ"
+        assert torch.equal(a, b) and torch.equal(a, c) and torch.equal(a, d), f"{n}: the layer forms differ"
+    assert torch.equal(Bs.y, Bp.y) and torch.equal(Bs.aq, Bp.aq) and torch.equal(Bs.asd, Bp.asd)
 
 
 def test_graph_capture_counts_once_and_replays_match_eager(decode):
