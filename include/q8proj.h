@@ -250,11 +250,15 @@ int q8_gemv_shared_multi_plus_f32(int m, const q8_weights* const* W, const int8_
  *   a_qs, a_sd: device buffers (K bytes, K/32 words; 16- and 4-byte aligned)
  *     that receive the row's q8_0 activation, as rmsnorm_quant writes it.
  *   m, W, ys, Wx, x2, yx: as q8_gemv_shared_multi_plus_f32 (m, W, y, Wx, x, yx).
+ *     Wx may be NULL: no f32-activation GEMV (x2 and yx are not read), as for
+ *     an LM head after the output norm.
  * Every output is bit-identical to rmsnorm_quant followed by
- * q8_gemv_shared_multi_plus_f32. The one launch serves the pair launch's
- * shapes (see there) with both parts non-empty; other shapes run those two
- * calls back to back (and count under their names). Errors: those of the two
- * calls, all checked before anything is launched; Q8_EINVAL for a NULL x or w.
+ * q8_gemv_shared_multi_plus_f32 (q8_gemv_shared_multi when Wx is NULL). The
+ * one launch serves the pair launch's shapes (see there; the grouped part at
+ * K in (2048, 8192], one row per wave), with the f32 part empty or absent or
+ * at K in (64, 512]; other shapes run those calls back to back (and count
+ * under their names). Errors: those of the calls, all checked before anything
+ * is launched; Q8_EINVAL for a NULL x or w.
  */
 int rmsnorm_quant_gemv_shared_multi_plus_f32(const float* x, const float* w, float eps, float* y, int8_t* a_qs,
                                              uint32_t* a_sd, int m, const q8_weights* const* W, float* const* ys,

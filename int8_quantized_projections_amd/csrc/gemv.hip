@@ -390,8 +390,8 @@ namespace {
 // A validated GEMV launch: its arguments and plan; `empty` when there is
 // nothing to compute.
 struct GemvJob {
-    GemvArgs a;
-    Plan p;
+    GemvArgs a{};
+    Plan p{};
     int K = 0, nb = 0;
     bool multi = false, empty = true;
 };
@@ -542,10 +542,15 @@ int step_nv(int K) {
 }
 
 // The one-launch step serves the pair kernel's shapes with one row per wave
-// (the grouped part's plan at one K chunk, K <= 8192) and both parts non-empty.
+// (the grouped part's plan at one K chunk, K <= 8192), with or without the
+// f32 part.
 bool step_supported(const GemvJob& j1, const GemvJob& j2) {
-    return !j1.empty && !j2.empty && pair_supported(j1.p, j2.p) && j1.p.rows == 1 && j1.K <= kMaxStepK &&
-           step_nv(j1.K) > 0 && (step_nv(j1.K) == 1) == (j1.p.nbl == 2);
+    const Plan& p1 = j1.p;
+    const Plan& p2 = j2.p;
+    const bool grouped_ok = !j1.empty && p1.lanes == 64 && (p1.nbl == 2 || p1.nbl == 4) && p1.rows == 1 &&
+                            j1.K <= kMaxStepK && step_nv(j1.K) > 0 && (step_nv(j1.K) == 1) == (p1.nbl == 2);
+    const bool f32_ok = j2.empty || (p2.nbl == 1 && p2.rows == 1 && (p2.lanes == 4 || p2.lanes == 8 || p2.lanes == 16));
+    return grouped_ok && f32_ok;
 }
 
 template <int NV, int NBL, int W2>
@@ -553,7 +558,7 @@ void launch_step3(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const flo
                   float* y, int8_t* a_qs, uint32_t* a_sd, const float* x2) {
     // the f32 part keeps its wave count; the grouped part takes the resident
     // 16-wave slots that the f32 part leaves (at least one workgroup)
-    const int64_t waves2 = j2.p.groups < kMaxWaves ? j2.p.groups : kMaxWaves;
+    const int64_t waves2 = j2.empty ? 0 : j2.p.groups < kMaxWaves ? j2.p.groups : kMaxWaves;
     const int wgs2 = (int)q8h::ceil_div(waves2, (int64_t)kStepWaves);
     const int64_t cap = kMaxWaves / kStepWaves - wgs2;
     const int64_t want = q8h::ceil_div(j1.p.groups, (int64_t)kStepWaves);
@@ -566,7 +571,7 @@ void launch_step3(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const flo
 template <int NV, int NBL>
 void launch_step2(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const float* x, const float* w, float eps,
                   float* y, int8_t* a_qs, uint32_t* a_sd, const float* x2) {
-    if (j2.p.lanes == 4)
+    if (j2.empty || j2.p.lanes == 4)  // no f32 part: any instance, with no workgroup for it
         launch_step3<NV, NBL, 4>(j1, j2, s, x, w, eps, y, a_qs, a_sd, x2);
     else if (j2.p.lanes == 8)
         launch_step3<NV, NBL, 8>(j1, j2, s, x, w, eps, y, a_qs, a_sd, x2);
@@ -648,7 +653,7 @@ int rmsnorm_quant_gemv_shared_multi_plus_f32(const float* x, const float* w, flo
     GemvJob j1, j2;
     int rc = prepare_multi(m, W, a_qs, a_sd, ys, 0, j1);
     if (rc) return rc;
-    if ((rc = prepare_f32(Wx, x2, yx, j2))) return rc;
+    if (Wx != nullptr && (rc = prepare_f32(Wx, x2, yx, j2))) return rc;  // Wx == NULL: no f32 part
     if (x == nullptr || w == nullptr) return Q8_EINVAL;
     if (!q8h::aligned(x, 16) || !q8h::aligned(w, 16) || !q8h::aligned(y, 16)) return Q8_EALIGN;
     const int64_t K = W[0]->k;
@@ -662,6 +667,7 @@ int rmsnorm_quant_gemv_shared_multi_plus_f32(const float* x, const float* w, flo
     }
     // other shapes: the producer, then the pair (or its two kernels)
     if ((rc = rmsnorm_quant(x, w, eps, y, 1, K, Q8_LAYOUT_ROW, a_qs, a_sd, stream))) return rc;
+    if (Wx == nullptr) return q8_gemv_shared_multi(m, W, a_qs, a_sd, ys, stream);
     return q8_gemv_shared_multi_plus_f32(m, W, a_qs, a_sd, ys, Wx, x2, yx, stream);
 }
 

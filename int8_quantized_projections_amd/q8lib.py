@@ -303,7 +303,8 @@ def rmsnorm_quant_gemv_shared_multi_plus_f32(x: torch.Tensor, w: torch.Tensor, e
                                              Wx: Q8Weights, x2: torch.Tensor, y=None, a_qs=None, a_sd=None, ys=None,
                                              yx=None, f32: bool = True):
     """rmsnorm_quant of the row x (ROW layout) and q8_gemv_shared_multi_plus_f32 of its consumers, in one
-    launch where the shapes allow. f32=False passes y = NULL. Returns (y, a_qs, a_sd, ys, yx)."""
+    launch where the shapes allow. Wx = None: no f32-activation GEMV (x2 is ignored, yx is None).
+    f32=False passes y = NULL. Returns (y, a_qs, a_sd, ys, yx)."""
     rows, k = _rows_k(x)
     if rows != 1:
         raise ValueError("the decode step normalizes one row")
@@ -314,14 +315,14 @@ def rmsnorm_quant_gemv_shared_multi_plus_f32(x: torch.Tensor, w: torch.Tensor, e
     m = len(Ws)
     if ys is None:
         ys = [torch.empty(W.n, dtype=torch.float32, device=x.device) for W in Ws]
-    if yx is None:
+    if yx is None and Wx is not None:
         yx = torch.empty(Wx.n, dtype=torch.float32, device=x.device)
     structs = [W.struct() for W in Ws]
     wps = (ctypes.POINTER(_Weights) * m)(*[ctypes.pointer(st) for st in structs])
     yps = (ctypes.c_void_p * m)(*[_ptr(t) for t in ys])
-    wx = Wx.struct()
+    wx = ctypes.byref(Wx.struct()) if Wx is not None else None  # None: no f32-activation GEMV
     _check(lib().rmsnorm_quant_gemv_shared_multi_plus_f32(_ptr(x), _ptr(w), eps, _ptr(y), _ptr(a_qs), _ptr(a_sd), m,
-                                                          wps, yps, ctypes.byref(wx), _ptr(x2), _ptr(yx),
+                                                          wps, yps, wx, _ptr(x2), _ptr(yx),
                                                           _stream(x.device)),
            "rmsnorm_quant_gemv_shared_multi_plus_f32")
     return y, a_qs, a_sd, ys, yx

@@ -282,7 +282,8 @@ def test_decode_step_rejects_before_launch(L):
     assert call(aq=None) == Q8_EINVAL                 # the activation buffers are required
     assert call(aq=f + 4) == Q8_EALIGN
     assert call(m=0) == Q8_EINVAL
-    assert call(WX=None) == Q8_EINVAL
+    assert call(WX=None, x=None) == Q8_EINVAL          # Wx = NULL (no f32 part) is valid; x is still required
+    assert call(WX=None, x2=None, yx=None, w=f + 4) == Q8_EALIGN
     assert call(WX=ctypes.byref(Wbig)) == Q8_ESHAPE   # f32 part K > 8192
     assert call(x2=f + 4) == Q8_EALIGN
     two = (ctypes.POINTER(q8lib._Weights) * 2)(ctypes.pointer(W), ctypes.pointer(W96))

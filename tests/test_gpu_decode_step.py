@@ -40,7 +40,9 @@ CASES = [
     ([1000, 24], 8192, 64, 128, True),
     ([77], 4128, 16, 128, True),
     ([64], 1024, 64, 128, False),          # K too narrow for the pair kernel: the two calls
-    ([300], 3584, 0, 128, False),          # empty f32 part
+    ([300], 3584, 0, 128, True),           # empty f32 part
+    ([4000, 77], 3584, None, None, True),  # no f32 part (Wx = NULL), as for an LM head
+    ([300], 1024, None, None, False),      # no f32 part, K too narrow: rmsnorm_quant + q8_gemv_shared_multi
     ([0, 0], 3584, 40, 128, False),        # empty grouped part
 ]
 
@@ -52,7 +54,7 @@ def _weights_or_empty(n, K, stream):
 
 def _inputs(Ns, K, Nx, Kx, base):
     Ws = [_weights_or_empty(n, K, base + 7 * i) for i, n in enumerate(Ns)]
-    Wx = _weights_or_empty(Nx, Kx, base + 50)
+    Wx = _weights_or_empty(Nx, Kx, base + 50) if Nx is not None else None
     w = synth.normal((K,), stream=base + 51, mean=1.0, std=0.1)
     return Ws, Wx, w
 
@@ -60,6 +62,8 @@ def _inputs(Ns, K, Nx, Kx, base):
 def _reference(x, w, Ws, Wx, x2):
     """rmsnorm_quant, then q8_gemv_shared_multi_plus_f32: the two-call form."""
     y, aq, asd = q8lib.rmsnorm_quant(x, w, EPS, ROW)
+    if Wx is None:
+        return y, aq, asd, q8lib.q8_gemv_shared_multi(Ws, aq, asd), None
     ys, yx = q8lib.q8_gemv_shared_multi_plus_f32(Ws, aq, asd, Wx, x2)
     return y, aq, asd, ys, yx
 
@@ -70,18 +74,20 @@ class Outs:
         nq, ns = q8lib.act_bytes(1, K, ROW)
         self.aq, self.asd = poisoned(nq, torch.int8), poisoned(ns // 4, torch.int32)
         self.ys = [poisoned(max(W.n, 1), torch.float32, 0xFF)[: W.n] for W in Ws]
-        self.yx = poisoned(max(Wx.n, 1), torch.float32, 0xFF)[: Wx.n]
+        self.yx = poisoned(max(Wx.n, 1), torch.float32, 0xFF)[: Wx.n] if Wx is not None else None
 
     def step(self, x, w, Ws, Wx, x2):
         q8lib.rmsnorm_quant_gemv_shared_multi_plus_f32(x, w, EPS, Ws, Wx, x2, self.y, self.aq, self.asd, self.ys,
                                                        self.yx)
 
     def all(self):
-        return [self.y, self.aq, self.asd, *self.ys, self.yx]
+        return [self.y, self.aq, self.asd, *self.ys] + ([self.yx] if self.yx is not None else [])
 
 
 def _assert_same(got, ref, what):
-    names = ["y", "a_qs", "a_sd"] + [f"y[{i}]" for i in range(len(got) - 4)] + ["yx"]
+    ref = [r for r in ref if r is not None]
+    assert len(got) == len(ref)
+    names = ["y", "a_qs", "a_sd"] + [f"y[{i}]" for i in range(len(got) - 3)]
     for g, r, n in zip(got, ref, names):
         assert torch.equal(g.reshape(-1).view(torch.int32 if g.dtype == torch.float32 else g.dtype),
                            r.reshape(-1).view(torch.int32 if r.dtype == torch.float32 else r.dtype)), \
@@ -90,13 +96,13 @@ def _assert_same(got, ref, what):
 
 @pytest.mark.parametrize("Ns,K,Nx,Kx,one", CASES)
 def test_step_bit_identical_to_two_calls(Ns, K, Nx, Kx, one):
-    Ws, Wx, wh = _inputs(Ns, K, Nx, Kx, 8100 + K + Kx)
+    Ws, Wx, wh = _inputs(Ns, K, Nx, Kx, 8100 + K + (Kx or 0))
     w = up(wh)
     o = Outs(K, Ws, Wx)
     # three different rows in a row: each call must read its own row's activation
     for r in range(3):
         xh = synth.normal((1, K), stream=8200 + 3 * K + r)
-        x, x2 = up(xh), up(synth.normal((Kx,), stream=8300 + Kx + r))
+        x, x2 = up(xh), (up(synth.normal((Kx,), stream=8300 + Kx + r)) if Kx else None)
         ref = _reference(x, w, Ws, Wx, x2)
         torch.cuda.synchronize()
         q8lib.launch_counts_reset()
@@ -107,8 +113,7 @@ def test_step_bit_identical_to_two_calls(Ns, K, Nx, Kx, one):
             assert c == {STEP: 1}, c
         else:
             assert c.get(STEP, 0) == 0 and c["rmsnorm_quant"] == 1, c
-        _assert_same([o.y, o.aq, o.asd, *o.ys, o.yx], [ref[0], ref[1], ref[2], *ref[3], ref[4]],
-                     f"{Ns}x{K} + {Nx}x{Kx}, row {r}")
+        _assert_same(o.all(), [ref[0], ref[1], ref[2], *ref[3], ref[4]], f"{Ns}x{K} + {Nx}x{Kx}, row {r}")
         if r == 0:  # the producer's output against the oracle
             y_ref = oracle.rmsnorm_f64(xh, wh, EPS)
             assert_rel(to_np(o.y), y_ref, 1e-5, f"rmsnorm 1x{K}")

@@ -165,13 +165,22 @@ def test_lm_head_full():
     x1 = synth.tensor(wl, "x1")
     x512 = synth.tensor(wl, "x512")
     W, wq, wd = workload_weights(wl, "W")
-    y1, _, _ = q8lib.rmsnorm_quant(up(x1), up(w), EPS, ROW)
+    y1, aq1, asd1 = q8lib.rmsnorm_quant(up(x1), up(w), EPS, ROW)
     y512, _, _ = q8lib.rmsnorm_quant(up(x512), up(w), EPS, PLANE)
     r1 = oracle.rmsnorm_f64(x1, w, EPS)
     r512 = oracle.rmsnorm_f64(x512, w, EPS)
     aq, asd, qo1, do1, _ = row_act(r1.astype(np.float32))
     logits = q8lib.q8_gemv(W, aq, asd)
+    # T=1 as the benchmark runs it: the output norm and the GEMV in one launch, bit-identical to
+    # rmsnorm_quant followed by q8_gemv on its output
+    two = q8lib.q8_gemv(W, aq1, asd1)
+    q8lib.launch_counts_reset()
+    s_y, s_aq, s_asd, (s_logits,), _ = q8lib.rmsnorm_quant_gemv_shared_multi_plus_f32(up(x1), up(w), EPS, [W], None,
+                                                                                     None)
     torch.cuda.synchronize()
+    assert {k: v for k, v in q8lib.launch_counts().items() if v} == {"rmsnorm_quant_gemv_shared_multi_plus_f32": 1}
+    assert torch.equal(s_y, y1) and torch.equal(s_aq, aq1) and torch.equal(s_asd, asd1)
+    assert torch.equal(s_logits.view(torch.int32), two.view(torch.int32)), "one-launch T=1 slice differs"
     assert_rel(to_np(y1), r1, 1e-5, "rmsnorm 1x3584")
     assert_rel(to_np(y512), r512, 1e-5, "rmsnorm 512x3584")
     ref, norm = oracle.gemv(wq, wd, qo1[0], do1[0])
