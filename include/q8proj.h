@@ -246,7 +246,10 @@ int q8_gemv_shared_multi_plus_f32(int m, const q8_weights* const* W, const int8_
  * quantizes the row into its own LDS and reads its activation from there, so
  * no workgroup waits for another; x and w are read from HBM once per XCD.
  *   x, w: device f32, K values each, 16-byte aligned. eps: as rmsnorm_quant.
- *   y: device f32 [K] for the normalized row, or NULL for none.
+ *   y: device f32 [K] for the normalized row, or NULL for none. y may be x
+ *     (in place); if y, a_qs or a_sd overlaps x or w, the call runs as the
+ *     two calls below instead of one launch. The GEMV outputs must not
+ *     overlap any input, as for the GEMV calls.
  *   a_qs, a_sd: device buffers (K bytes, K/32 words; 16- and 4-byte aligned)
  *     that receive the row's q8_0 activation, as rmsnorm_quant writes it.
  *   m, W, ys, Wx, x2, yx: as q8_gemv_shared_multi_plus_f32 (m, W, y, Wx, x, yx).

@@ -658,7 +658,18 @@ int rmsnorm_quant_gemv_shared_multi_plus_f32(const float* x, const float* w, flo
     if (!q8h::aligned(x, 16) || !q8h::aligned(w, 16) || !q8h::aligned(y, 16)) return Q8_EALIGN;
     const int64_t K = W[0]->k;
     const hipStream_t s = (hipStream_t)stream;
-    if (step_supported(j1, j2)) {
+    // One workgroup writes y and the activation while the others still read x
+    // and w, so the one launch needs those outputs apart from x and w (an
+    // in-place y = x runs as the two calls, which allow it).
+    auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb_) {
+        const char* pa = static_cast<const char*>(a);
+        const char* pb = static_cast<const char*>(b);
+        return a != nullptr && b != nullptr && pa < pb + nb_ && pb < pa + na;
+    };
+    const bool apart = !overlap(y, 4 * K, x, 4 * K) && !overlap(y, 4 * K, w, 4 * K) &&
+                       !overlap(a_qs, K, x, 4 * K) && !overlap(a_qs, K, w, 4 * K) &&
+                       !overlap(a_sd, K / 8, x, 4 * K) && !overlap(a_sd, K / 8, w, 4 * K);
+    if (apart && step_supported(j1, j2)) {
         if (j1.p.nbl == 2)
             launch_step2<1, 2>(j1, j2, s, x, w, eps, y, a_qs, a_sd, x2);
         else

@@ -164,3 +164,23 @@ def test_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         _assert_same(g_out.all(), ref, f"replay {i}")
     assert not torch.equal(e_out.ys[0], ref[3])
+
+
+def test_step_in_place_norm_runs_as_two_calls():
+    """y = x (an in-place norm): the one launch would let one workgroup overwrite x while the
+    others read it, so the call takes the two-call path, with the two calls' results."""
+    Ns, K, Nx, Kx = [4096, 512], 7168, 512, 128
+    Ws, Wx, wh = _inputs(Ns, K, Nx, Kx, 8600)
+    w = up(wh)
+    xh = synth.normal((1, K), stream=8601)
+    x2 = up(synth.normal((Kx,), stream=8602))
+    ref = _reference(up(xh), w, Ws, Wx, x2)
+    xin = up(xh)
+    o = Outs(K, Ws, Wx)
+    torch.cuda.synchronize()
+    q8lib.launch_counts_reset()
+    q8lib.rmsnorm_quant_gemv_shared_multi_plus_f32(xin, w, EPS, Ws, Wx, x2, xin, o.aq, o.asd, o.ys, o.yx)
+    torch.cuda.synchronize()
+    c = {k: v for k, v in q8lib.launch_counts().items() if v}
+    assert c.get(STEP, 0) == 0 and c["rmsnorm_quant"] == 1, c
+    _assert_same([xin, o.aq, o.asd, *o.ys, o.yx], [ref[0], ref[1], ref[2], *ref[3], ref[4]], "in place")
