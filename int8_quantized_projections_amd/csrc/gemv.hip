@@ -83,7 +83,7 @@ __device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __r
                                          int nb, int64_t groups, int64_t wave_id, int64_t nwaves) {
     constexpr int G = kWave / W;  // row slots per wave
     constexpr int CH = W * NBL;   // blocks per chunk
-    constexpr int kSeq = NBL < 2 ? NBL : 2;  // block columns per load step
+    constexpr int kSeq = 1;       // block columns per load step
     const int lane = threadIdx.x & (kWave - 1);
     const int slot = lane / W, u = lane % W;
     const int nchunks = (nb + CH - 1) / CH;
@@ -159,11 +159,12 @@ __device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __r
             bool inb[NBL];
 #pragma unroll
             for (int j = 0; j < NBL; ++j) inb[j] = ch * CH + u + j * W < nb;
-            // Block columns in steps of kSeq: a step's loads are issued, then consumed,
-            // before the next step's loads. Fewer bytes in flight per wave measured
-            // faster (5.24 -> 5.5 TB/s on the decode set): the requests of all waves
-            // then fall into fewer, denser address ranges. The per-row order of the
-            // accumulation is unchanged (j ascending).
+            // Block columns in steps of kSeq (one): a step's loads are issued, then
+            // consumed, before the next step's loads. Fewer bytes in flight per wave
+            // measured faster: 4 -> 2 columns per step took the decode set from 5.24
+            // to 5.5 TB/s, and 2 -> 1 the 152064x3584 GEMV from 101-102 to 98-99 us;
+            // the requests of all waves then fall into fewer, denser address ranges.
+            // The per-row order of the accumulation is unchanged (j ascending).
 #pragma unroll
             for (int j0 = 0; j0 < NBL; j0 += kSeq) {
                 uint4 w0[R][kSeq], w1[R][kSeq];
