@@ -261,7 +261,13 @@ __global__ __launch_bounds__(256) void k_gemv_pair(GemvArgs a1, const int8_t* __
 //    the polls alike, waits for that queue;
 //  - this form with the first weight loads issued before the producer's
 //    arithmetic: 32.9 us with the x and w loads after them, 35.7 us with the
-//    x and w loads first (then the registers spill).
+//    x and w loads first (then the registers spill); with each wave's first
+//    row copied into LDS by direct buffer -> LDS loads during the producer:
+//    33.1 us;
+//  - (with loads in steps of one block column; this form: 32.5 us) 224
+//    grouped workgroups, so that every wave takes exactly 6 rows: 34.4 us;
+//    all 256 workgroups on the grouped GEMV, the f32 GEMV's groups taken by
+//    the waves with one row fewer: 34.2 us after their rows, 33.1 us before.
 constexpr int kStepWaves = 16;    // waves per workgroup of the decode step
 constexpr int kMaxStepK = 8192;   // the grouped part's K: one chunk of 64 lanes x 4 blocks
 
