@@ -528,6 +528,41 @@ def bench_lm_head(D, reps):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle computing the decode step on this host
 # ---------------------------------------------------------------------------
+def cpu_gemv2048(budget_s, max_steps):
+    """The oracle on the single 2048x2048 GEMV at batch 1 (quantize of x, then the GEMV reference),
+    on all cores and on one thread: the same work as the GPU's q8_gemv_f32 launch."""
+    import oracle
+    import synth
+
+    wl = "gemv_2048"
+    x = synth.tensor(wl, "x").reshape(1, -1)
+    wq, wd, _ = oracle.quantize(synth.tensor(wl, "W"))  # untimed: weights are quantized once, at load
+
+    def one():
+        aq, ad, _ = oracle.quantize(x)
+        oracle.gemv(wq, wd, aq[0], ad[0])
+
+    def sample(budget):
+        one()  # warm
+        t0 = time.perf_counter()
+        k = 0
+        while k < max_steps and (time.perf_counter() - t0) < budget:
+            one()
+            k += 1
+        return k, time.perf_counter() - t0
+
+    b = gemv_f32_bytes(2048, 2048)
+    cores = oracle.num_threads()
+    k, dt = sample(budget_s)
+    oracle.set_threads(1)
+    k1, dt1 = sample(budget_s / 2)
+    oracle.set_threads(cores)
+    return {"value": b * k / dt / 1e9, "unit": "GB/s", "cores": cores, "us_per_gemv": dt / k * 1e6,
+            "sample": f"{k} GEMVs (quantize of x, then the f64 reference) in {dt:.1f} s",
+            "single_thread": {"value": b * k1 / dt1 / 1e9, "unit": "GB/s", "cores": 1,
+                              "us_per_gemv": dt1 / k1 * 1e6, "gemvs": k1}}
+
+
 def cpu_baseline(budget_s=10.0, max_steps=100000):
     import numpy as np
 
@@ -570,6 +605,8 @@ def cpu_baseline(budget_s=10.0, max_steps=100000):
     dt1 = time.perf_counter() - t1
     oracle.set_threads(cores)
     return {"value": step_bytes * k / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "per_core_GBps": step_bytes * k / dt / 1e9 / cores,
+            "gemv2048": cpu_gemv2048(budget_s / 4, max_steps),
             "sample": f"{k} full decode steps (rmsnorm + quantize, the six K=7168 GEMVs, quantize + GEMV "
                       f"for K=128; oracle references, f64) in {dt:.1f} s; "
                       "weights quantized once beforehand, untimed",
