@@ -440,6 +440,12 @@ def bench_prefill_swiglu(D, reps):
     b3 = b - T * K * 4
     out["swiglu_quant_plane64_no_f32"] = {**t3, "bytes": b3, "GBps": b3 / t3["mean_us"] / 1e3,
                                           "frac_hbm": b3 / t3["mean_us"] / 1e3 / HBM_PEAK_GBS}
+    # the unfused form's quantize pass: q8_quantize of the f32 y into the same plane (bit-identical
+    # to the fused plane), the activation quantize at bandwidth scale
+    t4 = stats(time_each(D, lambda i: q8.q8_quantize(y, q8.LAYOUT_PLANE64, pq, ps), reps))
+    b4 = quant_bytes(T, K, 1)
+    out["q8_quantize_plane64"] = {**t4, "bytes": b4, "GBps": b4 / t4["mean_us"] / 1e3,
+                                  "frac_hbm": b4 / t4["mean_us"] / 1e3 / HBM_PEAK_GBS}
     t2 = stats(time_each(D, lambda i: q8.q8_gemm(W, pq, ps, T, C), reps))
     out[f"q8_gemm_{N}x{K}"] = gemm_entry(t2, T, N, K)
     out["slice_launches"] = {"predicted": 2, "counted": counted_launches(q8, lambda: (

@@ -146,6 +146,85 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
     }
 }
 
+// ---------------------------------------------------------------------------
+// q8_quantize into PLANE64 for wide activations: each wave streams 4 KB runs
+// of one row (kRun consecutive units) instead of 1 KB pieces of four rows.
+// A workgroup covers 16 rows (one quarter of a 64-row group) by 4 units (32
+// chunks): wave w takes rows 4w..4w+3 of the quarter, and for each row the kRun
+// units in order. The quantized bytes are gathered in LDS and written as whole
+// 512-byte tile slices, as in k_elementwise. Work items are ordered (group,
+// 32-chunk column, quarter), so the four quarters of a tile run in consecutive
+// workgroups of one XCD. The quantize arithmetic is the same function as
+// every other producer's, so the plane has the same bits as k_elementwise's.
+// Measured (median us, k_elementwise -> this kernel): 3325x18944 62.2 -> 55.3
+// (5.2 -> 5.8 TB/s), 2048x16384 35.5 -> 31.6, 1024x18944 23.1 -> 22.2,
+// 3325x7168 26.8 -> 25.1 (1216 work items and more); 3325x3584 16.6 -> 18.7
+// and 512x3584 7.1 -> 11.0 (832 and 128): with a quarter of the workgroups it
+// loses once the grid no longer fills the chip, hence kRunMinWgs.
+// ---------------------------------------------------------------------------
+constexpr int kRun = 4;        // units per row per wave: 4 x 1 KB of f32
+constexpr int kQuarter = 16;   // rows per workgroup
+constexpr int kRunChunks = kRun * 8;  // chunks per workgroup column
+constexpr int kRunMinWgs = 1024;      // fewer work items take k_elementwise
+
+__global__ __launch_bounds__(256) void k_quantize_plane_runs(const float* __restrict__ x, int64_t rows, int K,
+                                                             int nb, int ncol, int8_t* __restrict__ qs,
+                                                             uint32_t* __restrict__ sd) {
+    const int64_t L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sub = lane & 7;
+    const int64_t g = L / (4 * (int64_t)ncol);  // 64-row group
+    const int col = (int)((L / 4) % ncol);      // 32-chunk column
+    const int quarter = (int)(L % 4);
+    constexpr int kCs = kQuarter * 8 + 8;  // words per chunk slice, padded against bank conflicts
+    __shared__ __attribute__((aligned(16))) uint32_t pq[kRunChunks * kCs];
+    __shared__ uint32_t psd[kRunChunks * kQuarter];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rs = 4 * wave + i;              // row in the quarter
+        const int rt = kQuarter * quarter + rs;   // row in the tile
+        const int64_t t = g * kGroup + rt;
+        const bool live = t < rows;
+#pragma unroll
+        for (int j = 0; j < kRun; ++j) {
+            // one unit per step: its load, then its quantize (loads from clamped,
+            // always-valid addresses; padded rows read row 0 and quantize zeros)
+            const int cc = 8 * j + (lane >> 3);   // chunk in the column
+            const int blk = kRunChunks * col + cc;
+            const int bc = blk < nb ? blk : nb - 1;
+            const float4 v = *reinterpret_cast<const float4*>(x + (live ? t : 0) * K + (int64_t)bc * kQK + sub * 4);
+            if (blk < nb) {  // whole 8-lane groups drop out together
+                const Quant8 r = quantize_block8(live ? v : make_float4(0.f, 0.f, 0.f, 0.f));
+                const int e = sub * 4;
+                const int h = ((e >> 4) ^ (rt >> 2) ^ (rt >> 3)) & 1;
+                pq[cc * kCs + rs * 8 + h * 4 + ((e & 15) >> 2)] = r.qs4;
+                if (sub == 0) psd[cc * kQuarter + rs] = r.sd;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+    const int tid = threadIdx.x;
+    // qs: 32 chunks x 512 bytes, 16 bytes per thread and pass
+#pragma unroll
+    for (int it = 0; it < kRunChunks / 8; ++it) {
+        const int cc = 8 * it + (tid >> 5);
+        const int c = kRunChunks * col + cc;
+        if (c < nb) {
+            const uint4 v4 = *reinterpret_cast<const uint4*>(&pq[cc * kCs + (tid & 31) * 4]);
+            store_stream(qs + (g * nb + c) * kTileBytes + kQuarter * quarter * kQK + (tid & 31) * 16, v4);
+        }
+    }
+    // scale words: 32 chunks x 16 rows
+#pragma unroll
+    for (int it = 0; it < kRunChunks * kQuarter / 256; ++it) {
+        const int i = 256 * it + tid;
+        const int cc = i / kQuarter, rs = i % kQuarter;
+        const int c = kRunChunks * col + cc;
+        if (c < nb) sd[(g * nb + c) * kGroup + kQuarter * quarter + rs] = psd[i];
+    }
+}
+
 // RMSNorm + quantize kernel: WPR waves per row (see dispatch_rms); the row
 // arithmetic is rmsnorm_rows in rmsnorm_row.h.
 template <int D, int NV, int WPR, int WAVES = kWavesPerWg>
@@ -204,6 +283,17 @@ int launch_elementwise(const float* a, const float* b, float* y, int64_t rows, i
     const int64_t wgs = q8h::ceil_div(units, kWavesPerWg * kUnr);
     if (wgs > INT32_MAX) return Q8_ESHAPE;
     const dim3 grid((unsigned)wgs);
+    if constexpr (!SWIGLU) {
+        if (qs != nullptr && layout == Q8_LAYOUT_PLANE64) {
+            const int ncol = (int)q8h::ceil_div(nb, kRunChunks);
+            const int64_t items = (tpad / kGroup) * ncol * 4;
+            if (items >= kRunMinWgs && items <= INT32_MAX) {
+                hipLaunchKernelGGL(k_quantize_plane_runs, dim3((unsigned)items), dim3(256), 0, s, a, rows, (int)k, nb,
+                                   ncol, qs, sd);
+                return q8h::launch_status(Q8_LAUNCH_QUANTIZE);
+            }
+        }
+    }
     if (qs == nullptr) {
         hipLaunchKernelGGL((k_elementwise<kDstNone, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, upr,
                            units, qs, sd);

@@ -75,6 +75,22 @@ def test_quantize_plane64_bit_exact_and_tail(T, K):
     check_plane_exact(qs, sd, x, f"q8_quantize PLANE64 {T}x{K}")
 
 
+@pytest.mark.parametrize("T,K", [(2000, 16480), (2048, 16384), (1250, 12320)])
+def test_quantize_plane64_wide_bit_exact_and_tail(T, K):
+    """Wide activations (1024 or more work items of 16 rows x 32 chunks) take the
+    4 KB-run kernel: a ragged last group and a partial last 32-chunk column,
+    and an exact fit, bit-exact with the oracle on poisoned buffers."""
+    x = synth.normal((T, K), stream=3290 + T)
+    qs, sd = quantize_dev(up(x), T, K, PLANE)
+    torch.cuda.synchronize()
+    check_plane_exact(qs, sd, x, f"q8_quantize PLANE64 {T}x{K}")
+    # the same plane from the fused producer's path (k_elementwise writes it for swiglu_quant)
+    y, q2, s2 = q8lib.swiglu_quant(up(x), up(np.ones_like(x)), PLANE)
+    q3, s3 = quantize_dev(y, T, K, PLANE)
+    torch.cuda.synchronize()
+    assert torch.equal(q2, q3) and torch.equal(s2, s3), "run-order plane differs from the fused producer's"
+
+
 def test_quantize_edge_values_bit_exact():
     """Ties, near-ties, zero blocks, f16-subnormal scales, f32-subnormal inputs."""
     rng = np.random.default_rng(7)
