@@ -147,8 +147,9 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
 }
 
 // ---------------------------------------------------------------------------
-// q8_quantize into PLANE64 for wide activations: each wave streams 4 KB runs
-// of one row (kRun consecutive units) instead of 1 KB pieces of four rows.
+// q8_quantize (SWIGLU: swiglu_quant first) into PLANE64 for wide activations:
+// each wave streams 4 KB runs of one row (kRun consecutive units) instead of
+// 1 KB pieces of four rows.
 // A workgroup covers 16 rows (one quarter of a 64-row group) by 4 units (32
 // chunks): wave w takes rows 4w..4w+3 of the quarter, and for each row the kRun
 // units in order. The quantized bytes are gathered in LDS and written as whole
@@ -160,14 +161,20 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
 // (5.2 -> 5.8 TB/s), 2048x16384 35.5 -> 31.6, 1024x18944 23.1 -> 22.2,
 // 3325x7168 26.8 -> 25.1 (1216 work items and more); 3325x3584 16.6 -> 18.7
 // and 512x3584 7.1 -> 11.0 (832 and 128): with a quarter of the workgroups it
-// loses once the grid no longer fills the chip, hence kRunMinWgs.
+// loses once the grid no longer fills the chip, hence kRunMinWgs. For
+// swiglu_quant it pays only without the f32 output (plane only: 3325x18944
+// 103.0 -> 101.4 us, 3325x7168 41.5 -> 38.3, 2048x16384 54.9 -> 53.6); with y
+// it measured slower (152.3 -> 165.5 us), so that form keeps k_elementwise.
+// SWIGLU computes silu(g) * u exactly as k_elementwise does (the same bits).
 // ---------------------------------------------------------------------------
 constexpr int kRun = 4;        // units per row per wave: 4 x 1 KB of f32
 constexpr int kQuarter = 16;   // rows per workgroup
 constexpr int kRunChunks = kRun * 8;  // chunks per workgroup column
 constexpr int kRunMinWgs = 1024;      // fewer work items take k_elementwise
 
-__global__ __launch_bounds__(256) void k_quantize_plane_runs(const float* __restrict__ x, int64_t rows, int K,
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void k_quantize_plane_runs(const float* __restrict__ x, const float* __restrict__ xb,
+                                                             float* __restrict__ y, int64_t rows, int K,
                                                              int nb, int ncol, int8_t* __restrict__ qs,
                                                              uint32_t* __restrict__ sd) {
     const int64_t L = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -192,8 +199,25 @@ __global__ __launch_bounds__(256) void k_quantize_plane_runs(const float* __rest
             const int cc = 8 * j + (lane >> 3);   // chunk in the column
             const int blk = kRunChunks * col + cc;
             const int bc = blk < nb ? blk : nb - 1;
-            const float4 v = *reinterpret_cast<const float4*>(x + (live ? t : 0) * K + (int64_t)bc * kQK + sub * 4);
+            const int64_t off = (live ? t : 0) * K + (int64_t)bc * kQK + sub * 4;
+            float4 v;
+            float4 wv;
+            if constexpr (SWIGLU) {
+                v = load_stream(x + off);
+                wv = load_stream(xb + off);
+            } else {
+                v = *reinterpret_cast<const float4*>(x + off);
+            }
             if (blk < nb) {  // whole 8-lane groups drop out together
+                if constexpr (SWIGLU) {
+                    float4 o;
+                    o.x = v.x * __builtin_amdgcn_rcpf(1.0f + __expf(-v.x)) * wv.x;
+                    o.y = v.y * __builtin_amdgcn_rcpf(1.0f + __expf(-v.y)) * wv.y;
+                    o.z = v.z * __builtin_amdgcn_rcpf(1.0f + __expf(-v.z)) * wv.z;
+                    o.w = v.w * __builtin_amdgcn_rcpf(1.0f + __expf(-v.w)) * wv.w;
+                    if (y != nullptr && live) store_stream(y + off, o);
+                    v = o;
+                }
                 const Quant8 r = quantize_block8(live ? v : make_float4(0.f, 0.f, 0.f, 0.f));
                 const int e = sub * 4;
                 const int h = ((e >> 4) ^ (rt >> 2) ^ (rt >> 3)) & 1;
@@ -283,14 +307,16 @@ int launch_elementwise(const float* a, const float* b, float* y, int64_t rows, i
     const int64_t wgs = q8h::ceil_div(units, kWavesPerWg * kUnr);
     if (wgs > INT32_MAX) return Q8_ESHAPE;
     const dim3 grid((unsigned)wgs);
-    if constexpr (!SWIGLU) {
+    // the 4 KB-run order: q8_quantize and the plane-only swiglu_quant (with an
+    // f32 output as well, swiglu_quant measured faster in k_elementwise's order)
+    if (!SWIGLU || y == nullptr) {
         if (qs != nullptr && layout == Q8_LAYOUT_PLANE64) {
             const int ncol = (int)q8h::ceil_div(nb, kRunChunks);
             const int64_t items = (tpad / kGroup) * ncol * 4;
             if (items >= kRunMinWgs && items <= INT32_MAX) {
-                hipLaunchKernelGGL(k_quantize_plane_runs, dim3((unsigned)items), dim3(256), 0, s, a, rows, (int)k, nb,
-                                   ncol, qs, sd);
-                return q8h::launch_status(Q8_LAUNCH_QUANTIZE);
+                hipLaunchKernelGGL(k_quantize_plane_runs<SWIGLU>, dim3((unsigned)items), dim3(256), 0, s, a, b, y,
+                                   rows, (int)k, nb, ncol, qs, sd);
+                return q8h::launch_status(SWIGLU ? Q8_LAUNCH_SWIGLU_QUANT : Q8_LAUNCH_QUANTIZE);
             }
         }
     }

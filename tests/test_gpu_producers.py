@@ -84,11 +84,17 @@ def test_quantize_plane64_wide_bit_exact_and_tail(T, K):
     qs, sd = quantize_dev(up(x), T, K, PLANE)
     torch.cuda.synchronize()
     check_plane_exact(qs, sd, x, f"q8_quantize PLANE64 {T}x{K}")
-    # the same plane from the fused producer's path (k_elementwise writes it for swiglu_quant)
-    y, q2, s2 = q8lib.swiglu_quant(up(x), up(np.ones_like(x)), PLANE)
+    # the same plane from the fused producer's path (k_elementwise writes it for swiglu_quant
+    # with an f32 output; the plane-only swiglu_quant takes the run order)
+    u = np.ones_like(x)
+    y, q2, s2 = q8lib.swiglu_quant(up(x), up(u), PLANE)
     q3, s3 = quantize_dev(y, T, K, PLANE)
+    nq, ns = q8lib.act_bytes(T, K, PLANE)
+    q4, s4 = poisoned(nq, torch.int8), poisoned(ns // 4, torch.int32)
+    q8lib.swiglu_quant(up(x), up(u), PLANE, None, q4, s4, f32=False)
     torch.cuda.synchronize()
     assert torch.equal(q2, q3) and torch.equal(s2, s3), "run-order plane differs from the fused producer's"
+    assert torch.equal(q2, q4) and torch.equal(s2, s4), "plane-only swiglu_quant differs from the fused one"
 
 
 def test_quantize_edge_values_bit_exact():
