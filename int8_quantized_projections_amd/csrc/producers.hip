@@ -148,40 +148,45 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
 
 // ---------------------------------------------------------------------------
 // q8_quantize (SWIGLU: swiglu_quant first) into PLANE64 for wide activations:
-// each wave streams 4 KB runs of one row (kRun consecutive units) instead of
-// 1 KB pieces of four rows.
-// A workgroup covers 16 rows (one quarter of a 64-row group) by 4 units (32
-// chunks): wave w takes rows 4w..4w+3 of the quarter, and for each row the kRun
-// units in order. The quantized bytes are gathered in LDS and written as whole
+// each wave streams runs of RUN consecutive units (RUN KB of f32) of one row
+// instead of 1 KB pieces of four rows.
+// A workgroup covers 16 rows (one quarter of a 64-row group) by RUN units
+// (8*RUN chunks): wave w takes rows 4w..4w+3 of the quarter, and for each row
+// the RUN units in order. The quantized bytes are gathered in LDS and written as whole
 // 512-byte tile slices, as in k_elementwise. Work items are ordered (group,
-// 32-chunk column, quarter), so the four quarters of a tile run in consecutive
+// 8*RUN-chunk column, quarter), so the four quarters of a tile run in consecutive
 // workgroups of one XCD. The quantize arithmetic is the same function as
 // every other producer's, so the plane has the same bits as k_elementwise's.
-// Measured (median us, k_elementwise -> this kernel): 3325x18944 62.2 -> 55.3
-// (5.2 -> 5.8 TB/s), 2048x16384 35.5 -> 31.6, 1024x18944 23.1 -> 22.2,
-// 3325x7168 26.8 -> 25.1 (1216 work items and more); 3325x3584 16.6 -> 18.7
-// and 512x3584 7.1 -> 11.0 (832 and 128): with a quarter of the workgroups it
+// Measured for q8_quantize (median us, k_elementwise -> 4 KB runs -> 2 KB
+// runs): 3325x18944 62.2 -> 55.3 -> 51.6 (5.2 -> 6.25 TB/s), 2048x16384
+// 35.5 -> 31.6 -> 30.7, 1024x18944 23.1 -> 22.2 -> 20.5, 3325x7168
+// 26.8 -> 25.1 -> 23.5, 3325x3584 16.6 -> 18.7 (832 items) -> 15.0 (1456).
+// With 4 KB runs 512x3584 took 11.0 us against 7.1: with fewer workgroups it
 // loses once the grid no longer fills the chip, hence kRunMinWgs. For
-// swiglu_quant it pays only without the f32 output (plane only: 3325x18944
-// 103.0 -> 101.4 us, 3325x7168 41.5 -> 38.3, 2048x16384 54.9 -> 53.6); with y
-// it measured slower (152.3 -> 165.5 us), so that form keeps k_elementwise.
+// swiglu_quant it pays only without the f32 output and with 4 KB runs (plane
+// only: 3325x18944 103.0 -> 101.4 us, 3325x7168 41.5 -> 38.3, 2048x16384
+// 54.9 -> 53.6; 2 KB runs 102-103 us); with y it measured slower (152.3 ->
+// 165.5 us with 4 KB runs, 156.5 with 2 KB), so that form keeps k_elementwise.
 // SWIGLU computes silu(g) * u exactly as k_elementwise does (the same bits).
 // ---------------------------------------------------------------------------
-constexpr int kRun = 4;        // units per row per wave: 4 x 1 KB of f32
-constexpr int kQuarter = 16;   // rows per workgroup
-constexpr int kRunChunks = kRun * 8;  // chunks per workgroup column
-constexpr int kRunMinWgs = 1024;      // fewer work items take k_elementwise
+constexpr int kQuarter = 16;      // rows per workgroup
+constexpr int kRunMinWgs = 1024;  // fewer work items take k_elementwise
+// units per row per wave (RUN x 1 KB of f32): 2 for q8_quantize, 4 for swiglu_quant
+constexpr int run_units(bool swiglu) { return swiglu ? 4 : 2; }
 
-template <bool SWIGLU>
+template <bool SWIGLU, int RUN = run_units(SWIGLU)>
 __global__ __launch_bounds__(256) void k_quantize_plane_runs(const float* __restrict__ x, const float* __restrict__ xb,
                                                              float* __restrict__ y, int64_t rows, int K,
                                                              int nb, int ncol, int8_t* __restrict__ qs,
                                                              uint32_t* __restrict__ sd) {
+    constexpr int kRun = RUN;
+    constexpr int kRunChunks = kRun * 8;  // chunks per workgroup column
+    static_assert(kRunChunks % 8 == 0 && kRunChunks * kQuarter % 256 == 0, "whole passes of the write-out");
     const int64_t L = xcd_contiguous(blockIdx.x, gridDim.x);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sub = lane & 7;
     const int64_t g = L / (4 * (int64_t)ncol);  // 64-row group
-    const int col = (int)((L / 4) % ncol);      // 32-chunk column
+    const int col = (int)((L / 4) % ncol);      // 8*RUN-chunk column
     const int quarter = (int)(L % 4);
     constexpr int kCs = kQuarter * 8 + 8;  // words per chunk slice, padded against bank conflicts
     __shared__ __attribute__((aligned(16))) uint32_t pq[kRunChunks * kCs];
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(256) void k_quantize_plane_runs(const float* __rest
     }
     __syncthreads();
     const int tid = threadIdx.x;
-    // qs: 32 chunks x 512 bytes, 16 bytes per thread and pass
+    // qs: 8*RUN chunks x 512 bytes, 16 bytes per thread and pass
 #pragma unroll
     for (int it = 0; it < kRunChunks / 8; ++it) {
         const int cc = 8 * it + (tid >> 5);
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(256) void k_quantize_plane_runs(const float* __rest
             store_stream(qs + (g * nb + c) * kTileBytes + kQuarter * quarter * kQK + (tid & 31) * 16, v4);
         }
     }
-    // scale words: 32 chunks x 16 rows
+    // scale words: 8*RUN chunks x 16 rows
 #pragma unroll
     for (int it = 0; it < kRunChunks * kQuarter / 256; ++it) {
         const int i = 256 * it + tid;
@@ -311,7 +316,7 @@ int launch_elementwise(const float* a, const float* b, float* y, int64_t rows, i
     // f32 output as well, swiglu_quant measured faster in k_elementwise's order)
     if (!SWIGLU || y == nullptr) {
         if (qs != nullptr && layout == Q8_LAYOUT_PLANE64) {
-            const int ncol = (int)q8h::ceil_div(nb, kRunChunks);
+            const int ncol = (int)q8h::ceil_div(nb, 8 * run_units(SWIGLU));
             const int64_t items = (tpad / kGroup) * ncol * 4;
             if (items >= kRunMinWgs && items <= INT32_MAX) {
                 hipLaunchKernelGGL(k_quantize_plane_runs<SWIGLU>, dim3((unsigned)items), dim3(256), 0, s, a, b, y,
