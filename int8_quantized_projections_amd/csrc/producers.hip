@@ -169,40 +169,46 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
 // 165.5 us with 4 KB runs, 156.5 with 2 KB), so that form keeps k_elementwise.
 // SWIGLU computes silu(g) * u exactly as k_elementwise does (the same bits).
 // ---------------------------------------------------------------------------
-constexpr int kQuarter = 16;      // rows per workgroup
+// Rows per workgroup (4 per wave). Whole 64-row groups per workgroup (16
+// waves; each workgroup then writes whole tiles, a contiguous 16-32 KB run of
+// the plane) measured slower: q8_quantize 3325x18944 51.0 -> 57.5 us,
+// swiglu_quant with y 152.6 -> 171.5 us.
+constexpr int kRunRows = 16;
 constexpr int kRunMinWgs = 1024;  // fewer work items take k_elementwise
 // units per row per wave (RUN x 1 KB of f32): 2 for q8_quantize, 4 for swiglu_quant
 constexpr int run_units(bool swiglu) { return swiglu ? 4 : 2; }
 
-template <bool SWIGLU, int RUN = run_units(SWIGLU)>
-__global__ __launch_bounds__(256) void k_quantize_plane_runs(const float* __restrict__ x, const float* __restrict__ xb,
-                                                             float* __restrict__ y, int64_t rows, int K,
-                                                             int nb, int ncol, int8_t* __restrict__ qs,
-                                                             uint32_t* __restrict__ sd) {
-    constexpr int kRun = RUN;
-    constexpr int kRunChunks = kRun * 8;  // chunks per workgroup column
-    static_assert(kRunChunks % 8 == 0 && kRunChunks * kQuarter % 256 == 0, "whole passes of the write-out");
+template <bool SWIGLU, int RUN = run_units(SWIGLU), int QR = kRunRows>
+__global__ __launch_bounds__(QR * 16) void k_quantize_plane_runs(const float* __restrict__ x,
+                                                                 const float* __restrict__ xb, float* __restrict__ y,
+                                                                 int64_t rows, int K, int nb, int ncol,
+                                                                 int8_t* __restrict__ qs, uint32_t* __restrict__ sd) {
+    constexpr int kChunks = RUN * 8;      // chunks per workgroup column
+    constexpr int kParts = kGroup / QR;   // workgroups per 64-row group and column
+    constexpr int kThreads = QR * 16;
+    static_assert(kGroup % QR == 0 && kChunks * 2 * QR % kThreads == 0 && kChunks * QR % kThreads == 0,
+                  "whole passes of the write-out");
     const int64_t L = xcd_contiguous(blockIdx.x, gridDim.x);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sub = lane & 7;
-    const int64_t g = L / (4 * (int64_t)ncol);  // 64-row group
-    const int col = (int)((L / 4) % ncol);      // 8*RUN-chunk column
-    const int quarter = (int)(L % 4);
-    constexpr int kCs = kQuarter * 8 + 8;  // words per chunk slice, padded against bank conflicts
-    __shared__ __attribute__((aligned(16))) uint32_t pq[kRunChunks * kCs];
-    __shared__ uint32_t psd[kRunChunks * kQuarter];
+    const int64_t g = L / (kParts * (int64_t)ncol);  // 64-row group
+    const int col = (int)((L / kParts) % ncol);      // 8*RUN-chunk column
+    const int part = (int)(L % kParts);
+    constexpr int kCs = QR * 8 + 8;  // words per chunk slice, padded against bank conflicts
+    __shared__ __attribute__((aligned(16))) uint32_t pq[kChunks * kCs];
+    __shared__ uint32_t psd[kChunks * QR];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int rs = 4 * wave + i;              // row in the quarter
-        const int rt = kQuarter * quarter + rs;   // row in the tile
+        const int rs = 4 * wave + i;        // row in the workgroup
+        const int rt = QR * part + rs;      // row in the tile
         const int64_t t = g * kGroup + rt;
         const bool live = t < rows;
 #pragma unroll
-        for (int j = 0; j < kRun; ++j) {
+        for (int j = 0; j < RUN; ++j) {
             // one unit per step: its load, then its quantize (loads from clamped,
             // always-valid addresses; padded rows read row 0 and quantize zeros)
             const int cc = 8 * j + (lane >> 3);   // chunk in the column
-            const int blk = kRunChunks * col + cc;
+            const int blk = kChunks * col + cc;
             const int bc = blk < nb ? blk : nb - 1;
             const int64_t off = (live ? t : 0) * K + (int64_t)bc * kQK + sub * 4;
             float4 v;
@@ -227,30 +233,31 @@ __global__ __launch_bounds__(256) void k_quantize_plane_runs(const float* __rest
                 const int e = sub * 4;
                 const int h = ((e >> 4) ^ (rt >> 2) ^ (rt >> 3)) & 1;
                 pq[cc * kCs + rs * 8 + h * 4 + ((e & 15) >> 2)] = r.qs4;
-                if (sub == 0) psd[cc * kQuarter + rs] = r.sd;
+                if (sub == 0) psd[cc * QR + rs] = r.sd;
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();
     const int tid = threadIdx.x;
-    // qs: 8*RUN chunks x 512 bytes, 16 bytes per thread and pass
+    // qs: 8*RUN chunks x (QR rows x 32 bytes), 16 bytes per thread and pass
 #pragma unroll
-    for (int it = 0; it < kRunChunks / 8; ++it) {
-        const int cc = 8 * it + (tid >> 5);
-        const int c = kRunChunks * col + cc;
+    for (int it = 0; it < kChunks * 2 * QR / kThreads; ++it) {
+        const int p = kThreads * it + tid;
+        const int cc = p / (2 * QR), q = p % (2 * QR);
+        const int c = kChunks * col + cc;
         if (c < nb) {
-            const uint4 v4 = *reinterpret_cast<const uint4*>(&pq[cc * kCs + (tid & 31) * 4]);
-            store_stream(qs + (g * nb + c) * kTileBytes + kQuarter * quarter * kQK + (tid & 31) * 16, v4);
+            const uint4 v4 = *reinterpret_cast<const uint4*>(&pq[cc * kCs + q * 4]);
+            store_stream(qs + (g * nb + c) * kTileBytes + QR * part * kQK + q * 16, v4);
         }
     }
-    // scale words: 8*RUN chunks x 16 rows
+    // scale words: 8*RUN chunks x QR rows
 #pragma unroll
-    for (int it = 0; it < kRunChunks * kQuarter / 256; ++it) {
-        const int i = 256 * it + tid;
-        const int cc = i / kQuarter, rs = i % kQuarter;
-        const int c = kRunChunks * col + cc;
-        if (c < nb) sd[(g * nb + c) * kGroup + kQuarter * quarter + rs] = psd[i];
+    for (int it = 0; it < kChunks * QR / kThreads; ++it) {
+        const int i = kThreads * it + tid;
+        const int cc = i / QR, rs = i % QR;
+        const int c = kChunks * col + cc;
+        if (c < nb) sd[(g * nb + c) * kGroup + QR * part + rs] = psd[i];
     }
 }
 
@@ -317,10 +324,10 @@ int launch_elementwise(const float* a, const float* b, float* y, int64_t rows, i
     if (!SWIGLU || y == nullptr) {
         if (qs != nullptr && layout == Q8_LAYOUT_PLANE64) {
             const int ncol = (int)q8h::ceil_div(nb, 8 * run_units(SWIGLU));
-            const int64_t items = (tpad / kGroup) * ncol * 4;
+            const int64_t items = (tpad / kGroup) * ncol * (kGroup / kRunRows);
             if (items >= kRunMinWgs && items <= INT32_MAX) {
-                hipLaunchKernelGGL(k_quantize_plane_runs<SWIGLU>, dim3((unsigned)items), dim3(256), 0, s, a, b, y,
-                                   rows, (int)k, nb, ncol, qs, sd);
+                hipLaunchKernelGGL(k_quantize_plane_runs<SWIGLU>, dim3((unsigned)items), dim3(kRunRows * 16), 0, s, a,
+                                   b, y, rows, (int)k, nb, ncol, qs, sd);
                 return q8h::launch_status(SWIGLU ? Q8_LAUNCH_SWIGLU_QUANT : Q8_LAUNCH_QUANTIZE);
             }
         }
