@@ -37,7 +37,8 @@ CASES = [
     ([300, 200], 3584, 100, 256, True),
     ([129], 2080, 33, 512, True),
     ([5, 0, 70], 4096, 7, 96, True),       # fewer rows than waves: most waves never wait
-    ([1000, 24], 8192, 64, 128, True),
+    ([1000, 24], 8192, 64, 128, True),     # the largest K of the one-launch form
+    ([200, 3], 8224, 40, 128, False),      # one block past it: rmsnorm_quant, then the GEMVs
     ([77], 4128, 16, 128, True),
     ([64], 1024, 64, 128, False),          # K too narrow for the pair kernel: the two calls
     ([300], 3584, 0, 128, True),           # empty f32 part
