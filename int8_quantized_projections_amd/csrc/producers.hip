@@ -67,6 +67,8 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
     // 8-chunk column, i.e. a 512-byte slice of each of 8 tiles. The quantized
     // bytes are gathered in LDS and written as whole slices (16 bytes per lane).
     constexpr int kSlice = kWavesPerWg * kUnr;  // rows per workgroup (16)
+    // the write-out below stores 16-row slices: 8 chunks x 512 bytes by 256 threads
+    static_assert(kSlice * kQK == 512 && kWavesPerWg * 64 == 8 * 32, "16-row slices, 256 threads");
     constexpr int kCs = kSlice * 8 + 8;  // words per chunk slice, padded against bank conflicts
     __shared__ __attribute__((aligned(16))) uint32_t pq[D == kDstPlane ? 8 * kCs : 1];
     __shared__ uint32_t psd[D == kDstPlane ? 8 * kSlice : 1];
