@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void k_gemv_pair(GemvArgs a1, const int8_t* __
 // Per workgroup that is 56 KB of L2 reads (x and w at K=7168; HBM serves them
 // once per XCD) and a few hundred instructions, with no dependency between
 // workgroups. Measured alternatives, per decode step (two launches: 33.9 us;
-// this form: 32.8 us):
+// this form, then with 240 grouped workgroups: 32.8 us):
 //  - one producer workgroup that the others wait for (a flag in memory, an
 //    agent-scope release and acquire, one poller per workgroup): 35.5 us, as
 //    every load issued behind the first rows' weight loads, the producer's and
@@ -264,10 +264,11 @@ __global__ __launch_bounds__(256) void k_gemv_pair(GemvArgs a1, const int8_t* __
 //    x and w loads first (then the registers spill); with each wave's first
 //    row copied into LDS by direct buffer -> LDS loads during the producer:
 //    33.1 us;
-//  - (with loads in steps of one block column; this form: 32.5 us) 224
-//    grouped workgroups, so that every wave takes exactly 6 rows: 34.4 us;
-//    all 256 workgroups on the grouped GEMV, the f32 GEMV's groups taken by
-//    the waves with one row fewer: 34.2 us after their rows, 33.1 us before.
+//  - (with loads in steps of one block column; this form with 240 grouped
+//    workgroups: 32.5 us) all 256 workgroups on the grouped GEMV, the f32
+//    GEMV's groups taken by the waves with one row fewer: 34.2 us after their
+//    rows, 33.1 us before. The grouped workgroup count is chosen in
+//    launch_step3 (the step's time follows the rows per wave).
 constexpr int kStepWaves = 16;    // waves per workgroup of the decode step
 constexpr int kMaxStepK = 8192;   // the grouped part's K: one chunk of 64 lanes x 4 blocks
 
@@ -563,16 +564,27 @@ bool step_supported(const GemvJob& j1, const GemvJob& j2) {
 template <int NV, int NBL, int W2>
 void launch_step3(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const float* x, const float* w, float eps,
                   float* y, int8_t* a_qs, uint32_t* a_sd, const float* x2) {
-    // the f32 part keeps its wave count; the grouped part takes the resident
-    // 16-wave slots that the f32 part leaves (at least one workgroup)
+    // The f32 part needs one wave per row group; the grouped part takes the
+    // resident 16-wave slots that leaves. When its rows take several rounds
+    // (rows per wave), it gets the fewest workgroups that keep the number of
+    // rounds, so every wave takes the same number of rows or one fewer, and the
+    // f32 part takes the slots this frees. Decode set (21,600 grouped rows):
+    // 225 grouped workgroups, 6 rows per wave: 31.8-31.9 us against 32.5 us
+    // with 240 (5 or 6 rows per wave), 34.3 with 224 (7 rows for 96 waves).
+    const int64_t slots = kMaxWaves / kStepWaves;
     const int64_t waves2 = j2.empty ? 0 : j2.p.groups < kMaxWaves ? j2.p.groups : kMaxWaves;
-    const int wgs2 = (int)q8h::ceil_div(waves2, (int64_t)kStepWaves);
-    const int64_t cap = kMaxWaves / kStepWaves - wgs2;
+    int64_t wgs2 = q8h::ceil_div(waves2, (int64_t)kStepWaves);
+    const int64_t cap = slots - wgs2 > 0 ? slots - wgs2 : 1;
     const int64_t want = q8h::ceil_div(j1.p.groups, (int64_t)kStepWaves);
-    const int64_t wgs1 = want < cap ? want : (cap > 0 ? cap : 1);
+    int64_t wgs1 = want;
+    if (want > cap) {
+        const int64_t rounds = q8h::ceil_div(j1.p.groups, cap * kStepWaves);
+        wgs1 = q8h::ceil_div(j1.p.groups, rounds * kStepWaves);
+        if (wgs2 > 0) wgs2 = slots - wgs1;
+    }
     const dim3 grid((unsigned)(wgs2 + wgs1));
     hipLaunchKernelGGL((k_decode_step<NV, NBL, 1, W2>), grid, dim3(kStepWaves * 64), 0, s, x, w, eps, y, a_qs, a_sd,
-                       j1.a, j1.K, j1.nb, j1.p.groups, j2.a, x2, j2.K, j2.nb, j2.p.groups, wgs2);
+                       j1.a, j1.K, j1.nb, j1.p.groups, j2.a, x2, j2.K, j2.nb, j2.p.groups, (int)wgs2);
 }
 
 template <int NV, int NBL>
