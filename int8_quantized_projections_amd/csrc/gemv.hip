@@ -338,7 +338,12 @@ Plan make_plan(int64_t total, int nb, int force_rows) {
     else
         p.rows = slots >= 16384 ? 4 : slots >= 2048 ? 2 : 1;
     p.groups = q8h::ceil_div(slots, p.rows);
-    const int64_t waves = p.groups < kMaxWaves ? p.groups : kMaxWaves;
+    // Persistent waves: the fewest that keep the minimal number of rounds (row
+    // groups per wave), so every wave takes the same number or one fewer.
+    // Decode set, grouped x6 (21,600 rows): 3,600 waves, 31.6-32.0 us against
+    // 32.2-32.7 with 4,096; the LM head is unchanged (4,002 against 4,096).
+    const int64_t rounds = q8h::ceil_div(p.groups, (int64_t)kMaxWaves);
+    const int64_t waves = p.groups < kMaxWaves ? p.groups : q8h::ceil_div(p.groups, rounds);
     p.workgroups = q8h::ceil_div(waves, kWavesPerWg);
     return p;
 }
