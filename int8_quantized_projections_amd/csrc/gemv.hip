@@ -162,8 +162,10 @@ __device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __r
             // Block columns in steps of kSeq (one): a step's loads are issued, then
             // consumed, before the next step's loads. Fewer bytes in flight per wave
             // measured faster: 4 -> 2 columns per step took the decode set from 5.24
-            // to 5.5 TB/s, and 2 -> 1 the 152064x3584 GEMV from 101-102 to 98-99 us;
-            // the requests of all waves then fall into fewer, denser address ranges.
+            // to 5.5 TB/s, and 2 -> 1 the 152064x3584 GEMV from 100-100.5 to 97-98 us,
+            // the decode pair from 33.1-33.5 to 31.6-31.8 us; the requests of all
+            // waves then fall into fewer, denser address ranges. (A short grid, the
+            // grouped x4 at 2.25 rows per wave, is the exception: 16.1 -> 17.6 us.)
             // The per-row order of the accumulation is unchanged (j ascending).
 #pragma unroll
             for (int j0 = 0; j0 < NBL; j0 += kSeq) {
@@ -314,6 +316,22 @@ int lanes_for(int nb) {
     return w;
 }
 
+// Persistent grids: the number of slots (waves, or workgroups of the decode
+// step) for `groups` units of work over at most `cap` slots. The fewest slots
+// that keep the minimal number of rounds (units per slot), so every slot takes
+// the same number or one fewer, when that removes at most 15% of the slots.
+// Decode set, grouped x6 (21,600 rows): 3,600 waves instead of 4,096, 32.2-32.7
+// -> 31.6-32.0 us; the one-launch step, 225 workgroups instead of 240,
+// 32.5 -> 31.8 us. Grouped x4 (9,216 rows) would drop to 3,072 waves (3 rows
+// each): the same time (17.6-17.7 us), and the limit keeps 4,096. The LM head
+// goes from 4,096 to 4,002 waves, unchanged in time.
+int64_t balanced_slots(int64_t groups, int64_t cap) {
+    if (groups <= cap) return groups;
+    const int64_t rounds = q8h::ceil_div(groups, cap);
+    const int64_t even = q8h::ceil_div(groups, rounds);
+    return even * 20 >= cap * 17 ? even : cap;
+}
+
 Plan make_plan(int64_t total, int nb, int force_rows) {
     Plan p;
     p.lanes = lanes_for(nb);
@@ -338,12 +356,7 @@ Plan make_plan(int64_t total, int nb, int force_rows) {
     else
         p.rows = slots >= 16384 ? 4 : slots >= 2048 ? 2 : 1;
     p.groups = q8h::ceil_div(slots, p.rows);
-    // Persistent waves: the fewest that keep the minimal number of rounds (row
-    // groups per wave), so every wave takes the same number or one fewer.
-    // Decode set, grouped x6 (21,600 rows): 3,600 waves, 31.6-32.0 us against
-    // 32.2-32.7 with 4,096; the LM head is unchanged (4,002 against 4,096).
-    const int64_t rounds = q8h::ceil_div(p.groups, (int64_t)kMaxWaves);
-    const int64_t waves = p.groups < kMaxWaves ? p.groups : q8h::ceil_div(p.groups, rounds);
+    const int64_t waves = p.groups < kMaxWaves ? p.groups : balanced_slots(p.groups, kMaxWaves);
     p.workgroups = q8h::ceil_div(waves, kWavesPerWg);
     return p;
 }
@@ -570,12 +583,10 @@ template <int NV, int NBL, int W2>
 void launch_step3(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const float* x, const float* w, float eps,
                   float* y, int8_t* a_qs, uint32_t* a_sd, const float* x2) {
     // The f32 part needs one wave per row group; the grouped part takes the
-    // resident 16-wave slots that leaves. When its rows take several rounds
-    // (rows per wave), it gets the fewest workgroups that keep the number of
-    // rounds, so every wave takes the same number of rows or one fewer, and the
-    // f32 part takes the slots this frees. Decode set (21,600 grouped rows):
-    // 225 grouped workgroups, 6 rows per wave: 31.8-31.9 us against 32.5 us
-    // with 240 (5 or 6 rows per wave), 34.3 with 224 (7 rows for 96 waves).
+    // resident 16-wave slots that leaves, balanced (balanced_slots: decode set,
+    // 225 workgroups, 6 rows per wave: 31.8-31.9 us against 32.5 us with 240,
+    // 5 or 6 rows per wave, and 34.3 with 224, 7 rows for 96 waves), and the
+    // f32 part takes the slots this frees.
     const int64_t slots = kMaxWaves / kStepWaves;
     const int64_t waves2 = j2.empty ? 0 : j2.p.groups < kMaxWaves ? j2.p.groups : kMaxWaves;
     int64_t wgs2 = q8h::ceil_div(waves2, (int64_t)kStepWaves);
@@ -583,8 +594,8 @@ void launch_step3(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const flo
     const int64_t want = q8h::ceil_div(j1.p.groups, (int64_t)kStepWaves);
     int64_t wgs1 = want;
     if (want > cap) {
-        const int64_t rounds = q8h::ceil_div(j1.p.groups, cap * kStepWaves);
-        wgs1 = q8h::ceil_div(j1.p.groups, rounds * kStepWaves);
+        // in workgroups: rows per workgroup round = kStepWaves
+        wgs1 = q8h::ceil_div(balanced_slots(j1.p.groups, cap * kStepWaves), (int64_t)kStepWaves);
         if (wgs2 > 0) wgs2 = slots - wgs1;
     }
     const dim3 grid((unsigned)(wgs2 + wgs1));
