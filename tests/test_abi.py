@@ -179,9 +179,19 @@ def test_gemv_rows_per_wave_threshold(L):
     p = q8lib.gemv_plan(4096, 128)
     assert p["lanes_per_row"] == 4 and p["rows_per_wave"] == 1
     assert q8lib.gemv_plan(0, 7168)["workgroups"] == 0
-    # the grid never exceeds the persistent cap, and covers small N fully
-    assert q8lib.gemv_plan(152064, 3584)["workgroups"] == 4096 // 4
+    # the grid never exceeds the persistent cap (4096 waves, 4 per workgroup) and covers
+    # small N fully; above the cap it takes the fewest waves that keep the number of
+    # rounds (rows per wave), when that removes at most 15% of the waves
     assert q8lib.gemv_plan(96, 7168)["workgroups"] == 24
+    assert q8lib.gemv_plan(4096, 7168)["workgroups"] == 1024     # one round, full grid
+    assert q8lib.gemv_plan(12288, 7168)["workgroups"] == 1024    # three full rounds
+    assert q8lib.gemv_plan(21600, 7168)["workgroups"] == 900     # 6 rounds: 3600 waves x 6 rows
+    assert q8lib.gemv_plan(152064, 3584)["workgroups"] == 1001   # 38 rounds: 4002 waves
+    assert q8lib.gemv_plan(9216, 7168)["workgroups"] == 1024     # 3072 waves would be 25% fewer
+    for n in (4097, 9216, 21600, 50000, 152064, 1 << 20):
+        waves = 4 * q8lib.gemv_plan(n, 7168)["workgroups"]
+        rounds = -(-n // 4096)
+        assert waves <= 4096 and -(-n // waves) == rounds, n  # never more rounds than the full grid
 
 
 def declared_launch_counters():
