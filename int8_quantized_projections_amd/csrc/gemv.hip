@@ -77,13 +77,13 @@ __device__ __forceinline__ int dot32(const uint4& w0, const uint4& w1, const uin
 // f32 (ax) and each lane quantizes the blocks it holds (one chunk only).
 // The GEMV of one wave: wave `wave_id` of `nwaves` takes row groups wave_id,
 // wave_id + nwaves, ...
-template <int W, int NBL, int R, bool MULTI, bool F32A>
+template <int W, int NBL, int R, bool MULTI, bool F32A, int KSEQ = 1>
 __device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __restrict__ aq,
                                          const uint32_t* __restrict__ asd, const float* __restrict__ ax, int K,
                                          int nb, int64_t groups, int64_t wave_id, int64_t nwaves) {
     constexpr int G = kWave / W;  // row slots per wave
     constexpr int CH = W * NBL;   // blocks per chunk
-    constexpr int kSeq = 1;       // block columns per load step
+    constexpr int kSeq = KSEQ < NBL ? KSEQ : NBL;  // block columns per load step
     const int lane = threadIdx.x & (kWave - 1);
     const int slot = lane / W, u = lane % W;
     const int nchunks = (nb + CH - 1) / CH;
@@ -159,7 +159,8 @@ __device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __r
             bool inb[NBL];
 #pragma unroll
             for (int j = 0; j < NBL; ++j) inb[j] = ch * CH + u + j * W < nb;
-            // Block columns in steps of kSeq (one): a step's loads are issued, then
+            // Block columns in steps of kSeq (one; two for short grids, see make_plan):
+            // a step's loads are issued, then
             // consumed, before the next step's loads. Fewer bytes in flight per wave
             // measured faster: 4 -> 2 columns per step took the decode set from 5.24
             // to 5.5 TB/s, and 2 -> 1 the 152064x3584 GEMV from 100-100.5 to 97-98 us,
@@ -216,11 +217,11 @@ __device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __r
     for (int64_t gi = wave_id + nwaves; gi < groups; gi += nwaves) body(gi, std::false_type{});
 }
 
-template <int W, int NBL, int R, bool MULTI, bool F32A = false>
+template <int W, int NBL, int R, bool MULTI, bool F32A = false, int KSEQ = 1>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs args, const int8_t* __restrict__ aq,
                                               const uint32_t* __restrict__ asd, const float* __restrict__ ax, int K,
                                               int nb, int64_t groups) {
-    gemv_run<W, NBL, R, MULTI, F32A>(args, aq, asd, ax, K, nb, groups,
+    gemv_run<W, NBL, R, MULTI, F32A, KSEQ>(args, aq, asd, ax, K, nb, groups,
                                      (int64_t)blockIdx.x * kWavesPerWg + (threadIdx.x >> 6),
                                      (int64_t)gridDim.x * kWavesPerWg);
 }
@@ -308,6 +309,7 @@ struct Plan {
     int rows;          // R
     int64_t groups;    // row groups
     int64_t workgroups;
+    int kseq;          // block columns per load step
 };
 
 int lanes_for(int nb) {
@@ -358,6 +360,14 @@ Plan make_plan(int64_t total, int nb, int force_rows) {
     p.groups = q8h::ceil_div(slots, p.rows);
     const int64_t waves = p.groups < kMaxWaves ? p.groups : balanced_slots(p.groups, kMaxWaves);
     p.workgroups = q8h::ceil_div(waves, kWavesPerWg);
+    // Loads in steps of one block column measured faster on every long grid;
+    // a short one (two or three rounds, the last at most half full) measured
+    // faster with two: the grouped x4 (9,216 rows over 4,096 waves) 17.5-17.7
+    // -> 16.1-16.2 us, while 12,288 rows (three full rounds) prefer one. The
+    // accumulation order is the same either way.
+    const int64_t rounds = q8h::ceil_div(p.groups, waves > 0 ? waves : 1);
+    const int64_t last = p.groups - (rounds - 1) * waves;
+    p.kseq = (nchunks == 1 && p.nbl >= 2 && rounds >= 2 && rounds <= 3 && 2 * last <= waves) ? 2 : 1;
     return p;
 }
 
@@ -368,7 +378,14 @@ void launch_r(const Plan& p, dim3 grid, hipStream_t s, const GemvArgs& a, const 
         hipLaunchKernelGGL((k_gemv<W, NBL, 4, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
     else if (p.rows == 2)
         hipLaunchKernelGGL((k_gemv<W, NBL, 2, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
-    else
+    else if constexpr (W == kWave && NBL >= 2 && !F32A) {
+        if (p.kseq == 2)
+            hipLaunchKernelGGL((k_gemv<W, NBL, 1, MULTI, F32A, 2>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb,
+                               p.groups);
+        else
+            hipLaunchKernelGGL((k_gemv<W, NBL, 1, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb,
+                               p.groups);
+    } else
         hipLaunchKernelGGL((k_gemv<W, NBL, 1, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
 }
 
