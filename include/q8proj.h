@@ -14,8 +14,26 @@
  *     calls ([P1] section 4: pass the buffer, do not cache it).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls enqueue their kernels on it and return without synchronising.
- *   - Arguments are validated on the host before anything is enqueued. On a
- *     negative return nothing was launched and no output byte was written.
+ *   - Arguments are validated on the host before anything is enqueued. On
+ *     Q8_EINVAL, Q8_ESHAPE or Q8_EALIGN nothing was launched and no output byte
+ *     was written. Q8_ELAUNCH means the HIP runtime refused a launch; the entry
+ *     points that may make two launches back to back (q8_gemv_shared_multi_plus_f32
+ *     and rmsnorm_quant_gemv_shared_multi_plus_f32 on shapes without their
+ *     one-launch kernel) can have enqueued the first when the second is refused,
+ *     and their outputs are then unspecified. Each launch's status is the one
+ *     hipLaunchKernel returns for it: an error the caller's own earlier HIP work
+ *     left pending (hipGetLastError) is never read, so it is not reported here.
+ *   - Inputs are finite f32 values; the results for NaN or infinity inputs are
+ *     unspecified (no fault). The producers' f32 outputs are within 1e-5
+ *     relative of the exact value plus an absolute 2^-126 (rmsnorm_quant), or
+ *     2^-126 * |up| + 2^-149 (swiglu_quant: silu(gate) is held to 2^-126 once it
+ *     leaves f32's normal range, gate below about -87.3, and a product below
+ *     that range rounds to f32's denormal step); the absolute parts matter only
+ *     below f32's normal range. For rmsnorm_quant this holds for every finite
+ *     x, including rows whose sum of squares overflows f32 (a rescaled second
+ *     pass). Outputs must be representable (|y| below f32's maximum). A block
+ *     whose d = amax/127 exceeds f16's maximum (amax above about 8.3e6) stores
+ *     d = +infinity, the IEEE conversion's result.
  *   - Outputs must not alias inputs. Two consumers that must not overwrite
  *     each other's quantized activation use separate buffers ([P1] s4).
  *   - Calls with zero rows (rows == 0, T == 0, N == 0) are valid no-ops.
@@ -40,8 +58,9 @@
  *                        Tokens rows <= t < 64*ntb are written as zero bytes
  *                        ([P2] s3.1, the padded tail is part of the plane).
  *
- *   Weights (struct q8_weights) are Q8_0 split into two planes:
- *     qs [N][K] int8 (row-major, 16-byte aligned) and d [N][K/32] f16 bits.
+ *   Weights (struct q8_weights, format Q8_WEIGHTS_Q8_0) are Q8_0 split into
+ *     two planes: qs [N][K] int8 (row-major, 16-byte aligned) and d [N][K/32]
+ *     f16 bits. q8_gemm also takes q4_K super-blocks (format Q8_WEIGHTS_Q4_K).
  *   q8_weights_repack converts GGUF Q8_0 blocks (34 bytes: f16 d at +0, int8
  *   qs[32] at +2, [P1] s2.1) into these planes once, at load time.
  */
@@ -55,25 +74,31 @@
 extern "C" {
 #endif
 
-#define Q8PROJ_ABI_VERSION 3
+#define Q8PROJ_ABI_VERSION 4
 
 /* return codes */
 #define Q8_OK 0
 #define Q8_EINVAL (-1)  /* NULL required pointer, unknown layout, m out of range */
 #define Q8_ESHAPE (-2)  /* negative size, K not a positive multiple of 32, K mismatch, ldc < N */
 #define Q8_EALIGN (-3)  /* pointer not aligned as documented */
-#define Q8_ELAUNCH (-4) /* the HIP runtime rejected a launch (hipGetLastError) */
+#define Q8_ELAUNCH (-4) /* the HIP runtime refused a launch (hipLaunchKernel's status for it) */
 #define Q8_ENODEV (-5)  /* no usable gfx950 device for the calling thread */
 
 /* activation layouts */
 #define Q8_LAYOUT_ROW 0
 #define Q8_LAYOUT_PLANE64 1
 
+/* weight formats (q8_weights.format) */
+#define Q8_WEIGHTS_Q8_0 0 /* Q8_0 split into the qs and d planes (every entry point) */
+#define Q8_WEIGHTS_Q4_K 1 /* q4_K super-blocks (struct q4k_weights below) at qs, d unused: q8_gemm only */
+
 typedef struct q8_weights {
     int64_t n;          /* output rows N */
-    int64_t k;          /* reduction width K, a positive multiple of 32 */
-    const int8_t* qs;   /* device, [N][K] int8, 16-byte aligned */
-    const uint16_t* d;  /* device, [N][K/32] f16 bits, 2-byte aligned */
+    int64_t k;          /* reduction width K, a positive multiple of 32 (of 256 for Q8_WEIGHTS_Q4_K) */
+    const int8_t* qs;   /* device, [N][K] int8, 16-byte aligned (Q4_K: the [N][K/256] x 144-byte blocks) */
+    const uint16_t* d;  /* device, [N][K/32] f16 bits, 2-byte aligned (Q4_K: not read) */
+    int64_t format;     /* Q8_WEIGHTS_Q8_0 (0, the value of a zero-initialised struct) or Q8_WEIGHTS_Q4_K;
+                           entry points that do not take a format return Q8_EINVAL */
 } q8_weights;
 
 /* q4_K weights ([P3] s2-s3.2): row-major [N][K/256] super-blocks of 144 bytes
@@ -140,6 +165,14 @@ const char* q8_launch_counter_name(int id);
  * Returns Q8_OK, Q8_EINVAL or Q8_ESHAPE.
  */
 int q8_act_bytes(int64_t rows, int64_t k, int layout, size_t* qs_bytes, size_t* sd_bytes);
+
+/*
+ * Bytes of a PLANE64 activation of T tokens of width K ([P2] s2.1-s2.2: the
+ * 64-token plane, ceil(T/64) groups of K/32 tiles of 2048 qs bytes and 64
+ * scale words): q8_act_bytes(T, K, Q8_LAYOUT_PLANE64, ...). Host only.
+ * Returns Q8_OK, Q8_EINVAL (NULL output) or Q8_ESHAPE.
+ */
+int q8_plane_bytes(int64_t t, int64_t k, size_t* qs_bytes, size_t* sd_bytes);
 
 /*
  * Activation quantize ([P1] s3-s3.1: quantize once per activation and pass
@@ -280,6 +313,8 @@ int q8_gemv_plan(int64_t total_rows, int64_t k, int rows_per_wave, int* lanes_pe
  * a_qs, a_sd: a PLANE64 activation of T tokens and width W->k.
  * C: [T][ldc] f32, row-major, ldc >= N; only columns n < N of rows t < T are
  * written. K <= 2^24 (Q8_ESHAPE otherwise).
+ * W->format Q8_WEIGHTS_Q4_K takes the q4_K weights at W->qs (as q4k_gemm
+ * below, the same bits); the launch counts under q8_gemm.
  */
 int q8_gemm(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t, float* c, int64_t ldc,
             void* stream);
@@ -318,6 +353,19 @@ int q4k_gemm(const q4k_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int
  * (device). Pure byte movement.
  */
 int q8_weights_repack(const void* gguf_blocks, int64_t n, int64_t k, int8_t* qs, uint16_t* d, void* stream);
+
+/*
+ * Measurement helper, not part of the projection path: the practical HBM read
+ * rate of this GPU, the ceiling the path's bandwidth figures are read against
+ * ([P1] s3: achieved bytes over time, against what the memory delivers). One
+ * launch streams `bytes` (a multiple of 16) of the device buffer buf (16-byte
+ * aligned) once, over `workgroups` workgroups of 256 lanes (1..65536), each
+ * lane reading 16-byte words grid-stride with loads_per_lane (1, 2 or 4) loads
+ * issued together; workgroup i writes an XOR of what it read to out[i]
+ * (device, `workgroups` words). Not counted by the launch counters.
+ */
+int q8_hbm_read_probe(const void* buf, int64_t bytes, int workgroups, int loads_per_lane, uint32_t* out,
+                      void* stream);
 
 #ifdef __cplusplus
 }

@@ -344,7 +344,7 @@ namespace {
 // Validation shared by q8_gemm and q8_gemm_shared_multi (the activation side is
 // checked by the caller).
 int check_member(const q8_weights* W, int64_t ldc, const float* c) {
-    if (W == nullptr) return Q8_EINVAL;
+    if (W == nullptr || W->format != Q8_WEIGHTS_Q8_0) return Q8_EINVAL;
     // K <= 2^24 keeps every in-tile byte offset of the weight copies in 32 bits.
     if (W->n < 0 || W->k <= 0 || (W->k % kQK) != 0 || W->k > ((int64_t)1 << 24)) return Q8_ESHAPE;
     if (ldc < W->n) return Q8_ESHAPE;
@@ -397,18 +397,26 @@ int launch_gemm(int counter, int m, const q8_weights* const* W, const int8_t* a_
     const int64_t tiles = n_tiles * q8h::ceil_div(t, kGroup);
     if (tiles > INT32_MAX) return Q8_ESHAPE;
     if (pairs)
-        hipLaunchKernelGGL(k_gemm<true>, dim3((unsigned)tiles), dim3(256), 0, stream, a_qs, a_sd, M, t,
+        q8h::launch_kernel(k_gemm<true>, dim3((unsigned)tiles), dim3(256), 0, stream, a_qs, a_sd, M, t,
                            (int)W[0]->k, nb, (int)n_tiles, tiles);
     else
-        hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)tiles), dim3(256), 0, stream, a_qs, a_sd, M, t,
+        q8h::launch_kernel(k_gemm<false>, dim3((unsigned)tiles), dim3(256), 0, stream, a_qs, a_sd, M, t,
                            (int)W[0]->k, nb, (int)n_tiles, tiles);
     return q8h::launch_status(counter);
 }
 
 }  // namespace
 
+// The q4_K GEMM (gemm_q4k.hip), counted under the given entry point.
+int launch_q4k_gemm(int counter, const q4k_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t,
+                    float* c, int64_t ldc, hipStream_t stream);
+
 extern "C" int q8_gemm(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t, float* c,
                        int64_t ldc, void* stream) {
+    if (W != nullptr && W->format == Q8_WEIGHTS_Q4_K) {
+        const q4k_weights w4 = {W->n, W->k, reinterpret_cast<const uint8_t*>(W->qs)};
+        return launch_q4k_gemm(Q8_LAUNCH_GEMM, &w4, a_qs, a_sd, t, c, ldc, (hipStream_t)stream);
+    }
     return launch_gemm(Q8_LAUNCH_GEMM, 1, &W, a_qs, a_sd, t, &c, &ldc, (hipStream_t)stream);
 }
 

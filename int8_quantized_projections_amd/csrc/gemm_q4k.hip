@@ -264,8 +264,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
 }  // namespace
 
-extern "C" int q4k_gemm(const q4k_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t, float* c,
-                        int64_t ldc, void* stream) {
+int launch_q4k_gemm(int counter, const q4k_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t,
+                    float* c, int64_t ldc, hipStream_t stream) {
     if (W == nullptr) return Q8_EINVAL;
     // K a multiple of 256 (whole super-blocks); K <= 2^24 keeps the in-tile offsets in 32 bits
     if (W->n < 0 || W->k <= 0 || (W->k % 256) != 0 || W->k > ((int64_t)1 << 24) || t < 0) return Q8_ESHAPE;
@@ -279,7 +279,12 @@ extern "C" int q4k_gemm(const q4k_weights* W, const int8_t* a_qs, const uint32_t
     const int64_t n_tiles = q8h::ceil_div(W->n, kBN);
     const int64_t tiles = n_tiles * q8h::ceil_div(t, kGroup);
     if (tiles > INT32_MAX) return Q8_ESHAPE;
-    hipLaunchKernelGGL(k_gemm_q4k, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, a_qs, a_sd, W->blocks,
-                       c, t, W->n, (int)W->k, nb, ldc, (int)n_tiles, tiles);
-    return q8h::launch_status(Q8_LAUNCH_Q4K_GEMM);
+    q8h::launch_kernel(k_gemm_q4k, dim3((unsigned)tiles), dim3(256), 0, stream, a_qs, a_sd, W->blocks, c, t, W->n,
+                       (int)W->k, nb, ldc, (int)n_tiles, tiles);
+    return q8h::launch_status(counter);
+}
+
+extern "C" int q4k_gemm(const q4k_weights* W, const int8_t* a_qs, const uint32_t* a_sd, int64_t t, float* c,
+                        int64_t ldc, void* stream) {
+    return launch_q4k_gemm(Q8_LAUNCH_Q4K_GEMM, W, a_qs, a_sd, t, c, ldc, (hipStream_t)stream);
 }

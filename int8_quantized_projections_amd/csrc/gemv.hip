@@ -375,18 +375,18 @@ template <int W, int NBL, bool MULTI, bool F32A>
 void launch_r(const Plan& p, dim3 grid, hipStream_t s, const GemvArgs& a, const int8_t* aq, const uint32_t* asd,
               const float* ax, int K, int nb) {
     if (p.rows == 4)
-        hipLaunchKernelGGL((k_gemv<W, NBL, 4, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
+        q8h::launch_kernel((k_gemv<W, NBL, 4, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
     else if (p.rows == 2)
-        hipLaunchKernelGGL((k_gemv<W, NBL, 2, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
+        q8h::launch_kernel((k_gemv<W, NBL, 2, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
     else if constexpr (W == kWave && NBL >= 2 && !F32A) {
         if (p.kseq == 2)
-            hipLaunchKernelGGL((k_gemv<W, NBL, 1, MULTI, F32A, 2>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb,
+            q8h::launch_kernel((k_gemv<W, NBL, 1, MULTI, F32A, 2>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb,
                                p.groups);
         else
-            hipLaunchKernelGGL((k_gemv<W, NBL, 1, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb,
+            q8h::launch_kernel((k_gemv<W, NBL, 1, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb,
                                p.groups);
     } else
-        hipLaunchKernelGGL((k_gemv<W, NBL, 1, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
+        q8h::launch_kernel((k_gemv<W, NBL, 1, MULTI, F32A>), grid, dim3(256), 0, s, a, aq, asd, ax, K, nb, p.groups);
 }
 
 template <bool MULTI, bool F32A>
@@ -419,7 +419,7 @@ void launch(const Plan& p, bool multi, hipStream_t s, const GemvArgs& a, const i
 }
 
 int check_weights(const q8_weights* w) {
-    if (w == nullptr) return Q8_EINVAL;
+    if (w == nullptr || w->format != Q8_WEIGHTS_Q8_0) return Q8_EINVAL;
     if (w->n < 0 || w->k <= 0 || (w->k % kQK) != 0 || w->k > ((int64_t)1 << 30)) return Q8_ESHAPE;
     if (w->n > 0 && (w->qs == nullptr || w->d == nullptr)) return Q8_EINVAL;
     if (!q8h::aligned(w->qs, 16) || !q8h::aligned(w->d, 2)) return Q8_EALIGN;
@@ -547,7 +547,7 @@ void launch_pair3(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const int
     const int64_t cap = kMaxWaves / kWavesPerWg - wgs2;
     const int64_t wgs1 = j1.p.workgroups < cap ? j1.p.workgroups : (cap > 0 ? cap : 1);
     const dim3 grid((unsigned)(wgs1 + wgs2));
-    hipLaunchKernelGGL((k_gemv_pair<64, NBL, R, W2>), grid, dim3(256), 0, s, j1.a, a_qs, a_sd, j1.K, j1.nb,
+    q8h::launch_kernel((k_gemv_pair<64, NBL, R, W2>), grid, dim3(256), 0, s, j1.a, a_qs, a_sd, j1.K, j1.nb,
                        j1.p.groups, j2.a, x, j2.K, j2.nb, j2.p.groups, wgs2);
 }
 
@@ -616,7 +616,7 @@ void launch_step3(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const flo
         if (wgs2 > 0) wgs2 = slots - wgs1;
     }
     const dim3 grid((unsigned)(wgs2 + wgs1));
-    hipLaunchKernelGGL((k_decode_step<NV, NBL, 1, W2>), grid, dim3(kStepWaves * 64), 0, s, x, w, eps, y, a_qs, a_sd,
+    q8h::launch_kernel((k_decode_step<NV, NBL, 1, W2>), grid, dim3(kStepWaves * 64), 0, s, x, w, eps, y, a_qs, a_sd,
                        j1.a, j1.K, j1.nb, j1.p.groups, j2.a, x2, j2.K, j2.nb, j2.p.groups, (int)wgs2);
 }
 

@@ -29,6 +29,23 @@ constexpr int kUnr = 4;
 constexpr int kSeq = 1;  // units per load step
 constexpr int kWavesPerWg = 4;
 
+// SwiGLU of one element ([P2] s3.2: silu(g) * u = g / (1 + e^-g) * u), written
+// with e = e^-|g|, which lies in (0, 1] for every finite g, so nothing overflows:
+// silu(g) = g / (1 + e) for g >= 0 and g * e / (1 + e) for g < 0. exp2f keeps
+// results below 2^-126 as denormals (the compiler scales the hardware exp2
+// there). silu(g) is then within about 6e-8 * |g| relative (the rounding of the
+// exponent argument) plus a few ulp while it is an f32 normal, and within
+// 2^-126 absolute below that (gate below about -87.3).
+__device__ __forceinline__ float swiglu1(float g, float u) {
+    const float e = exp2f(-fabsf(g) * 1.44269504088896341f);
+    const float r = __builtin_amdgcn_rcpf(1.0f + e);
+    return (g >= 0.0f ? g : g * e) * r * u;
+}
+
+__device__ __forceinline__ float4 swiglu4(const float4& g, const float4& u) {
+    return make_float4(swiglu1(g.x, u.x), swiglu1(g.y, u.y), swiglu1(g.z, u.z), swiglu1(g.w, u.w));
+}
+
 template <int D, bool SWIGLU>
 __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a, const float* __restrict__ b,
                                                      float* __restrict__ y, int64_t rows, int K, int nb, int upr,
@@ -98,13 +115,7 @@ __global__ __launch_bounds__(256) void k_elementwise(const float* __restrict__ a
             const int u = u0 + i;
             if (blk[u] >= nb) continue;  // whole 8-lane groups drop out together
             if constexpr (SWIGLU) {
-                // [P2] s3.2: silu(g) * u = g / (1 + e^-g) * u, with the hardware exp2 and
-                // reciprocal (each within about an ulp; the f32 output is checked to 1e-5).
-                float4 o;
-                o.x = v[i].x * __builtin_amdgcn_rcpf(1.0f + __expf(-v[i].x)) * w[i].x;
-                o.y = v[i].y * __builtin_amdgcn_rcpf(1.0f + __expf(-v[i].y)) * w[i].y;
-                o.z = v[i].z * __builtin_amdgcn_rcpf(1.0f + __expf(-v[i].z)) * w[i].z;
-                o.w = v[i].w * __builtin_amdgcn_rcpf(1.0f + __expf(-v[i].w)) * w[i].w;
+                const float4 o = swiglu4(v[i], w[i]);
                 if (y != nullptr && live[u])  // y == NULL: quantized output only
                     store_stream(y + trow[u] * K + (int64_t)blk[u] * kQK + sub * 4, o);
                 v[i] = o;
@@ -223,11 +234,7 @@ __global__ __launch_bounds__(QR * 16) void k_quantize_plane_runs(const float* __
             }
             if (blk < nb) {  // whole 8-lane groups drop out together
                 if constexpr (SWIGLU) {
-                    float4 o;
-                    o.x = v.x * __builtin_amdgcn_rcpf(1.0f + __expf(-v.x)) * wv.x;
-                    o.y = v.y * __builtin_amdgcn_rcpf(1.0f + __expf(-v.y)) * wv.y;
-                    o.z = v.z * __builtin_amdgcn_rcpf(1.0f + __expf(-v.z)) * wv.z;
-                    o.w = v.w * __builtin_amdgcn_rcpf(1.0f + __expf(-v.w)) * wv.w;
+                    const float4 o = swiglu4(v, wv);
                     if (y != nullptr && live) store_stream(y + off, o);
                     v = o;
                 }
@@ -328,20 +335,20 @@ int launch_elementwise(const float* a, const float* b, float* y, int64_t rows, i
             const int ncol = (int)q8h::ceil_div(nb, 8 * run_units(SWIGLU));
             const int64_t items = (tpad / kGroup) * ncol * (kGroup / kRunRows);
             if (items >= kRunMinWgs && items <= INT32_MAX) {
-                hipLaunchKernelGGL(k_quantize_plane_runs<SWIGLU>, dim3((unsigned)items), dim3(kRunRows * 16), 0, s, a,
+                q8h::launch_kernel(k_quantize_plane_runs<SWIGLU>, dim3((unsigned)items), dim3(kRunRows * 16), 0, s, a,
                                    b, y, rows, (int)k, nb, ncol, qs, sd);
                 return q8h::launch_status(SWIGLU ? Q8_LAUNCH_SWIGLU_QUANT : Q8_LAUNCH_QUANTIZE);
             }
         }
     }
     if (qs == nullptr) {
-        hipLaunchKernelGGL((k_elementwise<kDstNone, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, upr,
+        q8h::launch_kernel((k_elementwise<kDstNone, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, upr,
                            units, qs, sd);
     } else if (layout == Q8_LAYOUT_ROW) {
-        hipLaunchKernelGGL((k_elementwise<kDstRow, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, upr,
+        q8h::launch_kernel((k_elementwise<kDstRow, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, upr,
                            units, qs, sd);
     } else {
-        hipLaunchKernelGGL((k_elementwise<kDstPlane, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, upr,
+        q8h::launch_kernel((k_elementwise<kDstPlane, SWIGLU>), grid, dim3(256), 0, s, a, b, y, rows, (int)k, nb, upr,
                            units, qs, sd);
     }
     return q8h::launch_status(SWIGLU ? Q8_LAUNCH_SWIGLU_QUANT : Q8_LAUNCH_QUANTIZE);
@@ -353,7 +360,7 @@ void launch_rms(int nv, dim3 grid, hipStream_t s, const float* x, const float* w
     const dim3 block(WAVES * 64);
 #define Q8_RMS_CASE(N)                                                                                           \
     case N:                                                                                                      \
-        hipLaunchKernelGGL((k_rmsnorm<D, N, WPR, WAVES>), grid, block, 0, s, x, w, eps, y, rows, tpad, k, nb, qs, \
+        q8h::launch_kernel((k_rmsnorm<D, N, WPR, WAVES>), grid, block, 0, s, x, w, eps, y, rows, tpad, k, nb, qs, \
                            sd);                                                                                  \
         break;
     // at 1024 threads a lane has 128 VGPRs: more than 8 float4 per lane take the two-pass form
@@ -378,7 +385,7 @@ void launch_rms(int nv, dim3 grid, hipStream_t s, const float* x, const float* w
             }
             [[fallthrough]];
         default:
-            hipLaunchKernelGGL((k_rmsnorm<D, 0, WPR, WAVES>), grid, block, 0, s, x, w, eps, y, rows, tpad, k, nb, qs,
+            q8h::launch_kernel((k_rmsnorm<D, 0, WPR, WAVES>), grid, block, 0, s, x, w, eps, y, rows, tpad, k, nb, qs,
                                sd);
     }
 #undef Q8_RMS_CASE
@@ -463,6 +470,10 @@ int q8_act_bytes(int64_t rows, int64_t k, int layout, size_t* qs_bytes, size_t* 
     return Q8_OK;
 }
 
+int q8_plane_bytes(int64_t t, int64_t k, size_t* qs_bytes, size_t* sd_bytes) {
+    return q8_act_bytes(t, k, Q8_LAYOUT_PLANE64, qs_bytes, sd_bytes);
+}
+
 int q8_quantize(const float* x, int64_t rows, int64_t k, int layout, int8_t* qs, uint32_t* sd, void* stream) {
     int rc = check_act_shape(rows, k);
     if (rc) return rc;
@@ -511,7 +522,7 @@ int q8_weights_repack(const void* gguf_blocks, int64_t n, int64_t k, int8_t* qs,
     if (!q8h::aligned(gguf_blocks, 2) || !q8h::aligned(qs, 16) || !q8h::aligned(d, 2)) return Q8_EALIGN;
     const int64_t nblocks = n * (k / kQK);
     if (nblocks == 0) return Q8_OK;
-    hipLaunchKernelGGL(k_repack, dim3((unsigned)q8h::ceil_div(nblocks, 256)), dim3(256), 0, (hipStream_t)stream,
+    q8h::launch_kernel(k_repack, dim3((unsigned)q8h::ceil_div(nblocks, 256)), dim3(256), 0, (hipStream_t)stream,
                        reinterpret_cast<const uint16_t*>(gguf_blocks), nblocks, qs, d);
     return q8h::launch_status(Q8_LAUNCH_WEIGHTS_REPACK);
 }

@@ -10,6 +10,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <tuple>
 
 #include "q8proj.h"
 
@@ -195,10 +196,32 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 // Launch counters of the entry points (Q8_LAUNCH_* ids), process-wide.
 inline std::atomic<int64_t> launches[Q8_LAUNCH_COUNTERS];
 
-// Status of the launch just made by the calling thread; a successful launch
-// adds one to the entry point's counter.
+// The first failure among the calling thread's launches since its last
+// launch_status() (hipSuccess: none).
+inline thread_local hipError_t launch_error = hipSuccess;
+
+// Every kernel launch of the library: hipLaunchKernel returns the status of
+// this launch alone, which is kept for launch_status(). The thread's pending
+// HIP error (hipGetLastError) is never read, so an error left by the caller's
+// own earlier work is not reported as the library's.
+template <typename... P, typename... A>
+inline void launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem, hipStream_t s, A... args) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<P...> vals{static_cast<P>(args)...};
+    void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1];
+    std::apply([&ptrs](auto&... v) {
+        size_t i = 0;
+        ((ptrs[i++] = static_cast<void*>(&v)), ...);
+    }, vals);
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, s);
+    if (e != hipSuccess && launch_error == hipSuccess) launch_error = e;
+}
+
+// Status of the launches the calling thread made since the last call; on
+// success one launch is added to the entry point's counter.
 inline int launch_status(int counter) {
-    hipError_t e = hipGetLastError();
+    const hipError_t e = launch_error;
+    launch_error = hipSuccess;
     if (e != hipSuccess) return Q8_ELAUNCH;
     launches[counter].fetch_add(1, std::memory_order_relaxed);
     return Q8_OK;

@@ -64,6 +64,13 @@ __device__ __forceinline__ void store_quant(const Quant8& r, int64_t t, int c, i
 // read hits L2), with the same per-lane order of the sum of squares.
 // Every wave of the workgroup must call it (WPR > 1 combines the waves'
 // partial sums through LDS behind a barrier). qs and sd may point to LDS.
+//
+// A row whose f32 sum of squares overflows (|x| above about 1.8e19 / sqrt(K))
+// takes a second pass over x * 2^-80, whose squares stay in range for any
+// finite x and K <= 2^24: y = (x * 2^-80) * rsqrt(sum((x * 2^-80)^2) / K +
+// eps * 2^-160) * w, the same value. Rows whose sum is finite keep the first
+// pass's bits. Every wave of a workgroup takes the second reduction when any
+// of its rows needs it, so the barrier inside is reached by all of them.
 // ---------------------------------------------------------------------------
 template <int D, int NV, int WPR, int WAVES>
 __device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const float* __restrict__ w, float eps,
@@ -73,6 +80,7 @@ __device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const 
     constexpr int kRowsPerWg = WAVES / WPR;
     constexpr int kStride = kWave * WPR;  // float4 stride between a lane's elements
     __shared__ float part[WAVES];
+    __shared__ float part2[WAVES];  // the rescaled second pass (a separate buffer: no wait for the first's readers)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = wg * kRowsPerWg + wave / WPR;
     const int li = (wave % WPR) * kWave + lane;  // lane index inside the row
@@ -84,18 +92,31 @@ __device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const 
     // y == NULL: the quantized output only, no f32 row is written
     float4* __restrict__ y4 = y != nullptr ? reinterpret_cast<float4*>(y + (live ? t : 0) * K) : nullptr;
 
-    auto row_sum = [&](float ss) {
+    // The row's total, and (any_big) whether the total of any row of the
+    // workgroup is not finite -- the same answer in every wave of the workgroup.
+    auto row_sum = [&](float ss, float* buf, bool& any_big) {
         ss = wave_sum(ss);
         if constexpr (WPR > 1) {
-            if (lane == 0) part[wave] = ss;
+            if (lane == 0) buf[wave] = ss;
             __syncthreads();
-            const int w0 = (wave / WPR) * WPR;
-            ss = part[w0];
+            float mine = 0.0f;
+            bool any = false;
 #pragma unroll
-            for (int i = 1; i < WPR; ++i) ss += part[w0 + i];
+            for (int r = 0; r < kRowsPerWg; ++r) {
+                float tot = buf[r * WPR];
+#pragma unroll
+                for (int i = 1; i < WPR; ++i) tot += buf[r * WPR + i];
+                any |= !__builtin_isfinite(tot);
+                if (r == wave / WPR) mine = tot;
+            }
+            any_big = any;
+            return mine;
+        } else {
+            any_big = !__builtin_isfinite(ss);
+            return ss;
         }
-        return ss;
     };
+    constexpr float kDown = 0x1p-80f;  // the second pass's prescale
 
     if constexpr (NV > 0) {
         float4 v[NV], wv[NV];
@@ -119,18 +140,36 @@ __device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const 
             ss = fmaf(v[k].z, v[k].z, ss);
             ss = fmaf(v[k].w, v[k].w, ss);
         }
-        ss = row_sum(ss);
-        if (!inrow) return;
+        bool any_big;
+        ss = row_sum(ss, part, any_big);
         // [P2] s3.2: scale = rsqrt(ss/d + eps), y = x * scale * w.
-        const float scale = rsqrtf(ss / (float)K + eps);
+        float scale = rsqrtf(ss / (float)K + eps), pre = 1.0f;
+        if (any_big) {  // uniform over the workgroup
+            float s2 = 0.0f;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const float a = v[k].x * kDown, b = v[k].y * kDown, c = v[k].z * kDown, d = v[k].w * kDown;
+                s2 = fmaf(a, a, s2);
+                s2 = fmaf(b, b, s2);
+                s2 = fmaf(c, c, s2);
+                s2 = fmaf(d, d, s2);
+            }
+            bool unused;
+            s2 = row_sum(s2, part2, unused);
+            if (!__builtin_isfinite(ss)) {
+                scale = rsqrtf(s2 / (float)K + eps * kDown * kDown);
+                pre = kDown;
+            }
+        }
+        if (!inrow) return;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = li + kStride * k;
-            float4 o;
-            o.x = v[k].x * scale * wv[k].x;
-            o.y = v[k].y * scale * wv[k].y;
-            o.z = v[k].z * scale * wv[k].z;
-            o.w = v[k].w * scale * wv[k].w;
+            float4 o;  // pre is 1 (exact) unless the row took the second pass
+            o.x = v[k].x * pre * scale * wv[k].x;
+            o.y = v[k].y * pre * scale * wv[k].y;
+            o.z = v[k].z * pre * scale * wv[k].z;
+            o.w = v[k].w * pre * scale * wv[k].w;
             if (y4 != nullptr && live && idx < n4) store_stream(reinterpret_cast<float*>(y4 + idx), o);
             v[k] = o;  // zero for padded rows and past K
         }
@@ -155,9 +194,29 @@ __device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const 
                 ss = fmaf(a.w, a.w, ss);
             }
         }
-        ss = row_sum(ss);
+        bool any_big;
+        ss = row_sum(ss, part, any_big);
+        float scale = rsqrtf(ss / (float)K + eps), pre = 1.0f;
+        if (any_big) {  // uniform over the workgroup
+            float s2 = 0.0f;
+            if (live) {
+                for (int idx = li; idx < n4; idx += kStride) {
+                    const float4 a = x4[idx];
+                    const float p = a.x * kDown, q = a.y * kDown, r = a.z * kDown, u = a.w * kDown;
+                    s2 = fmaf(p, p, s2);
+                    s2 = fmaf(q, q, s2);
+                    s2 = fmaf(r, r, s2);
+                    s2 = fmaf(u, u, s2);
+                }
+            }
+            bool unused;
+            s2 = row_sum(s2, part2, unused);
+            if (!__builtin_isfinite(ss)) {
+                scale = rsqrtf(s2 / (float)K + eps * kDown * kDown);
+                pre = kDown;
+            }
+        }
         if (!inrow) return;
-        const float scale = rsqrtf(ss / (float)K + eps);
         const int steps = (n4 + kStride - 1) / kStride;
         for (int k = 0; k < steps; ++k) {
             const int idx = li + kStride * k;
@@ -166,10 +225,10 @@ __device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const 
             const float4 wq = w4[ic];
             float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
             if (live && idx < n4) {
-                o.x = a.x * scale * wq.x;
-                o.y = a.y * scale * wq.y;
-                o.z = a.z * scale * wq.z;
-                o.w = a.w * scale * wq.w;
+                o.x = a.x * pre * scale * wq.x;
+                o.y = a.y * pre * scale * wq.y;
+                o.z = a.z * pre * scale * wq.z;
+                o.w = a.w * pre * scale * wq.w;
                 if (y4 != nullptr) store_stream(reinterpret_cast<float*>(y4 + idx), o);
             }
             if constexpr (D != kDstNone) {

@@ -29,8 +29,13 @@ class Q8Error(RuntimeError):
         super().__init__(f"{where}: {_ERRORS.get(code, code)} ({_lib_strerror(code)})")
 
 
+WEIGHTS_Q8_0 = 0
+WEIGHTS_Q4_K = 1
+
+
 class _Weights(ctypes.Structure):
-    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("qs", ctypes.c_void_p), ("d", ctypes.c_void_p)]
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("qs", ctypes.c_void_p), ("d", ctypes.c_void_p),
+                ("format", ctypes.c_int64)]
 
 
 _lib = None
@@ -50,6 +55,7 @@ def lib() -> ctypes.CDLL:
             "q8_abi_version": ([], ci),
             "q8_strerror": ([ci], ctypes.c_char_p),
             "q8_act_bytes": ([i64, i64, ci, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)], ci),
+            "q8_plane_bytes": ([i64, i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)], ci),
             "q8_quantize": ([vp, i64, i64, ci, vp, vp, vp], ci),
             "rmsnorm_quant": ([vp, vp, ctypes.c_float, vp, i64, i64, ci, vp, vp, vp], ci),
             "swiglu_quant": ([vp, vp, vp, i64, i64, ci, vp, vp, vp], ci),
@@ -66,6 +72,7 @@ def lib() -> ctypes.CDLL:
             "q8_gemv_shared_multi_plus_f32": ([ci, ctypes.POINTER(wp), vp, vp, ctypes.POINTER(vp), wp, vp, vp, vp], ci),
             "rmsnorm_quant_gemv_shared_multi_plus_f32": ([vp, vp, ctypes.c_float, vp, vp, vp, ci, ctypes.POINTER(wp),
                                                           ctypes.POINTER(vp), wp, vp, vp, vp], ci),
+            "q8_hbm_read_probe": ([vp, i64, ci, ci, vp, vp], ci),
             "q8_launch_counts": ([ctypes.POINTER(i64), ci], ci),
             "q8_launch_counts_reset": ([], None),
             "q8_launch_counter_name": ([ci], ctypes.c_char_p),
@@ -104,6 +111,36 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return t.data_ptr()
 
 
+# Buffer checks, made before anything reaches the library: a tensor of the wrong
+# element type, or one too short for what the kernel reads or writes, is refused
+# here (the C ABI sees only a pointer and cannot tell).
+_I8 = (torch.int8, torch.uint8)
+_I16 = (torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.int16,)
+_I32 = (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
+
+
+def _need(t: torch.Tensor | None, name: str, dtypes, numel: int) -> torch.Tensor | None:
+    """t (or None) must have one of `dtypes` and at least `numel` elements."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {numel} needed")
+    return t
+
+
+def _need_act(qs, sd, rows: int, k: int, layout: int, what: str) -> None:
+    """Quantized-activation buffers of rows x k in `layout`: int8 qs and 32-bit scale words."""
+    nq, ns = act_bytes(rows, k, layout)
+    _need(qs, f"{what} qs", _I8, nq)
+    _need(sd, f"{what} sd", _I32, ns // 4)
+
+
 # ---------------------------------------------------------------------------
 # Buffers
 # ---------------------------------------------------------------------------
@@ -123,6 +160,14 @@ def launch_counts() -> dict[str, int]:
 
 def launch_counts_reset() -> None:
     lib().q8_launch_counts_reset()
+
+
+def plane_bytes(t: int, k: int) -> tuple[int, int]:
+    """(qs bytes, scale-word bytes) of a PLANE64 activation of t tokens of width k."""
+    q = ctypes.c_size_t()
+    s = ctypes.c_size_t()
+    _check(lib().q8_plane_bytes(t, k, ctypes.byref(q), ctypes.byref(s)), "q8_plane_bytes")
+    return q.value, s.value
 
 
 def act_bytes(rows: int, k: int, layout: int) -> tuple[int, int]:
@@ -153,7 +198,13 @@ class Q8Weights:
         return self.qs.shape[1]
 
     def struct(self) -> _Weights:
-        return _Weights(self.n, self.k, _ptr(self.qs), _ptr(self.d))
+        if self.qs.dim() != 2 or self.d.dim() != 2:
+            raise ValueError("Q8Weights: qs [N, K] and d [N, K/32] must be 2-D")
+        _need(self.qs, "Q8Weights.qs", _I8, 0)
+        _need(self.d, "Q8Weights.d", _I16, 0)
+        if self.k % QK != 0 or tuple(self.d.shape) != (self.n, self.k // QK):
+            raise ValueError(f"Q8Weights: d is {tuple(self.d.shape)}, expected ({self.n}, {self.k // QK})")
+        return _Weights(self.n, self.k, _ptr(self.qs), _ptr(self.d), WEIGHTS_Q8_0)
 
     def rows(self, start: int, stop: int) -> "Q8Weights":
         """A band of output rows (a pointer offset and a smaller N)."""
@@ -175,9 +226,16 @@ class Q4KWeights:
         return self.blocks.shape[0]
 
     def struct(self) -> _Q4KWeights:
-        assert self.blocks.dtype == torch.uint8 and self.blocks.is_contiguous()
-        assert self.blocks.shape[1] == self.k // 256 * 144
+        _need(self.blocks, "Q4KWeights.blocks", torch.uint8, 0)
+        if self.k % 256 != 0 or self.blocks.dim() != 2 or self.blocks.shape[1] != self.k // 256 * 144:
+            raise ValueError(f"Q4KWeights: blocks {tuple(self.blocks.shape)} do not hold K={self.k} "
+                             "in 144-byte super-blocks of 256 values")
         return _Q4KWeights(self.n, self.k, _ptr(self.blocks))
+
+    def q8_struct(self) -> _Weights:
+        """The same weights as a q8_weights descriptor of format Q8_WEIGHTS_Q4_K (for q8_gemm)."""
+        w = self.struct()
+        return _Weights(w.n, w.k, w.blocks, None, WEIGHTS_Q4_K)
 
 
 def q4k_gemm(W: Q4KWeights, a_qs: torch.Tensor, a_sd: torch.Tensor, t: int, C=None, ldc: int | None = None):
@@ -186,6 +244,8 @@ def q4k_gemm(W: Q4KWeights, a_qs: torch.Tensor, a_sd: torch.Tensor, t: int, C=No
         C = torch.empty((t, W.n), dtype=torch.float32, device=a_qs.device)
     if ldc is None:
         ldc = C.shape[-1] if C.dim() > 1 else W.n
+    _need_act(a_qs, a_sd, t, W.k, LAYOUT_PLANE64, "q4k_gemm")
+    _need(C, "C", torch.float32, (t - 1) * ldc + W.n if t > 0 else 0)
     ws = W.struct()
     _check(lib().q4k_gemm(ctypes.byref(ws), _ptr(a_qs), _ptr(a_sd), t, _ptr(C), ldc, _stream(a_qs.device)),
            "q4k_gemm")
@@ -194,7 +254,7 @@ def q4k_gemm(W: Q4KWeights, a_qs: torch.Tensor, a_sd: torch.Tensor, t: int, C=No
 
 def q8_weights_repack(blocks: torch.Tensor, n: int, k: int) -> Q8Weights:
     """GGUF Q8_0 blocks (device uint8, N*K/32*34 bytes) -> Q8Weights (one-time, at load)."""
-    assert blocks.dtype == torch.uint8 and blocks.numel() == n * (k // QK) * 34
+    _need(blocks, "blocks", torch.uint8, n * (k // QK) * 34)
     qs = torch.empty((n, k), dtype=torch.int8, device=blocks.device)
     d = torch.empty((n, k // QK), dtype=torch.int16, device=blocks.device)
     _check(lib().q8_weights_repack(_ptr(blocks), n, k, _ptr(qs), _ptr(d), _stream(blocks.device)),
@@ -206,15 +266,22 @@ def q8_weights_repack(blocks: torch.Tensor, n: int, k: int) -> Q8Weights:
 # Producers
 # ---------------------------------------------------------------------------
 def _rows_k(x: torch.Tensor) -> tuple[int, int]:
+    """(rows, K) of an activation: [K] is one row, [rows, K] a matrix; other ranks are refused."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"expected a torch.Tensor, got {type(x).__name__}")
     if x.dim() == 1:
         return 1, x.shape[0]
-    return x.shape[0], x.shape[-1]
+    if x.dim() == 2:
+        return x.shape[0], x.shape[1]
+    raise ValueError(f"activations are [K] or [rows, K]; got shape {tuple(x.shape)}")
 
 
 def q8_quantize(x: torch.Tensor, layout: int = LAYOUT_ROW, qs=None, sd=None):
     rows, k = _rows_k(x)
+    _need(x, "x", torch.float32, rows * k)
     if qs is None:
         qs, sd = alloc_act(rows, k, layout, x.device)
+    _need_act(qs, sd, rows, k, layout, "q8_quantize")
     _check(lib().q8_quantize(_ptr(x), rows, k, layout, _ptr(qs), _ptr(sd), _stream(x.device)), "q8_quantize")
     return qs, sd
 
@@ -223,12 +290,17 @@ def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float, layout: int = LA
                   quant: bool = True, f32: bool = True):
     """f32=False passes y = NULL: only the quantized activation is written (returned y is None)."""
     rows, k = _rows_k(x)
+    _need(x, "x", torch.float32, rows * k)
+    _need(w, "w", torch.float32, k)
     if y is None and f32:
         y = torch.empty_like(x)
     if quant and qs is None:
         qs, sd = alloc_act(rows, k, layout, x.device)
     if not quant:
         qs = sd = None
+    _need(y, "y", torch.float32, rows * k)
+    if qs is not None or sd is not None:
+        _need_act(qs, sd, rows, k, layout, "rmsnorm_quant")
     _check(lib().rmsnorm_quant(_ptr(x), _ptr(w), eps, _ptr(y), rows, k, layout, _ptr(qs), _ptr(sd),
                                _stream(x.device)), "rmsnorm_quant")
     return y, qs, sd
@@ -238,12 +310,19 @@ def swiglu_quant(gate: torch.Tensor, up: torch.Tensor, layout: int = LAYOUT_ROW,
                  quant: bool = True, f32: bool = True):
     """f32=False passes y = NULL: only the quantized activation is written (returned y is None)."""
     rows, k = _rows_k(gate)
+    _need(gate, "gate", torch.float32, rows * k)
+    _need(up, "up", torch.float32, rows * k)
+    if tuple(up.shape) != tuple(gate.shape):
+        raise ValueError(f"gate {tuple(gate.shape)} and up {tuple(up.shape)} differ")
     if y is None and f32:
         y = torch.empty_like(gate)
     if quant and qs is None:
         qs, sd = alloc_act(rows, k, layout, gate.device)
     if not quant:
         qs = sd = None
+    _need(y, "y", torch.float32, rows * k)
+    if qs is not None or sd is not None:
+        _need_act(qs, sd, rows, k, layout, "swiglu_quant")
     _check(lib().swiglu_quant(_ptr(gate), _ptr(up), _ptr(y), rows, k, layout, _ptr(qs), _ptr(sd),
                               _stream(gate.device)), "swiglu_quant")
     return y, qs, sd
@@ -252,9 +331,16 @@ def swiglu_quant(gate: torch.Tensor, up: torch.Tensor, layout: int = LAYOUT_ROW,
 # ---------------------------------------------------------------------------
 # Consumers
 # ---------------------------------------------------------------------------
+def _need_row_act(a_qs, a_sd, k: int, what: str) -> None:
+    _need(a_qs, f"{what} a_qs", _I8, k)
+    _need(a_sd, f"{what} a_sd", _I32, k // QK)
+
+
 def q8_gemv(W: Q8Weights, a_qs: torch.Tensor, a_sd: torch.Tensor, y=None) -> torch.Tensor:
     if y is None:
         y = torch.empty(W.n, dtype=torch.float32, device=a_qs.device)
+    _need_row_act(a_qs, a_sd, W.k, "q8_gemv")
+    _need(y, "y", torch.float32, W.n)
     ws = W.struct()
     _check(lib().q8_gemv(ctypes.byref(ws), _ptr(a_qs), _ptr(a_sd), _ptr(y), _stream(a_qs.device)), "q8_gemv")
     return y
@@ -264,9 +350,19 @@ def q8_gemv_f32(W: Q8Weights, x: torch.Tensor, y=None) -> torch.Tensor:
     """GEMV on an f32 activation [K] quantized inside the launch (K <= 8192)."""
     if y is None:
         y = torch.empty(W.n, dtype=torch.float32, device=x.device)
+    _need(x, "x", torch.float32, W.k)
+    _need(y, "y", torch.float32, W.n)
     ws = W.struct()
     _check(lib().q8_gemv_f32(ctypes.byref(ws), _ptr(x), _ptr(y), _stream(x.device)), "q8_gemv_f32")
     return y
+
+
+def _need_members(Ws, ys) -> None:
+    """Members of a grouped GEMV: one output per weight matrix, each long enough."""
+    if len(Ws) == 0 or len(ys) != len(Ws):
+        raise ValueError(f"{len(Ws)} weight matrices and {len(ys)} outputs")
+    for i, (W, y) in enumerate(zip(Ws, ys)):
+        _need(y, f"y[{i}]", torch.float32, W.n)
 
 
 def q8_gemv_shared_multi(Ws: list[Q8Weights], a_qs: torch.Tensor, a_sd: torch.Tensor, ys=None,
@@ -274,6 +370,8 @@ def q8_gemv_shared_multi(Ws: list[Q8Weights], a_qs: torch.Tensor, a_sd: torch.Te
     m = len(Ws)
     if ys is None:
         ys = [torch.empty(W.n, dtype=torch.float32, device=a_qs.device) for W in Ws]
+    _need_members(Ws, ys)
+    _need_row_act(a_qs, a_sd, Ws[0].k, "q8_gemv_shared_multi")
     structs = [W.struct() for W in Ws]
     wps = (ctypes.POINTER(_Weights) * m)(*[ctypes.pointer(s) for s in structs])
     yps = (ctypes.c_void_p * m)(*[_ptr(y) for y in ys])
@@ -290,6 +388,10 @@ def q8_gemv_shared_multi_plus_f32(Ws: list[Q8Weights], a_qs: torch.Tensor, a_sd:
         ys = [torch.empty(W.n, dtype=torch.float32, device=a_qs.device) for W in Ws]
     if yx is None:
         yx = torch.empty(Wx.n, dtype=torch.float32, device=x.device)
+    _need_members(Ws, ys)
+    _need_row_act(a_qs, a_sd, Ws[0].k, "q8_gemv_shared_multi_plus_f32")
+    _need(x, "x", torch.float32, Wx.k)
+    _need(yx, "yx", torch.float32, Wx.n)
     structs = [W.struct() for W in Ws]
     wps = (ctypes.POINTER(_Weights) * m)(*[ctypes.pointer(st) for st in structs])
     yps = (ctypes.c_void_p * m)(*[_ptr(y) for y in ys])
@@ -317,6 +419,14 @@ def rmsnorm_quant_gemv_shared_multi_plus_f32(x: torch.Tensor, w: torch.Tensor, e
         ys = [torch.empty(W.n, dtype=torch.float32, device=x.device) for W in Ws]
     if yx is None and Wx is not None:
         yx = torch.empty(Wx.n, dtype=torch.float32, device=x.device)
+    _need(x, "x", torch.float32, k)
+    _need(w, "w", torch.float32, k)
+    _need(y, "y", torch.float32, k)
+    _need_row_act(a_qs, a_sd, k, "rmsnorm_quant_gemv_shared_multi_plus_f32")
+    _need_members(Ws, ys)
+    if Wx is not None:
+        _need(x2, "x2", torch.float32, Wx.k)
+        _need(yx, "yx", torch.float32, Wx.n)
     structs = [W.struct() for W in Ws]
     wps = (ctypes.POINTER(_Weights) * m)(*[ctypes.pointer(st) for st in structs])
     yps = (ctypes.c_void_p * m)(*[_ptr(t) for t in ys])
@@ -337,12 +447,15 @@ def gemv_plan(total_rows: int, k: int, rows_per_wave: int = 0) -> dict:
     return {"lanes_per_row": lanes.value, "rows_per_wave": rows.value, "workgroups": wg.value}
 
 
-def q8_gemm(W: Q8Weights, a_qs: torch.Tensor, a_sd: torch.Tensor, t: int, C=None, ldc: int | None = None):
+def q8_gemm(W, a_qs: torch.Tensor, a_sd: torch.Tensor, t: int, C=None, ldc: int | None = None):
+    """C [t, N] = W x PLANE64 activation; W is Q8Weights, or Q4KWeights (format Q8_WEIGHTS_Q4_K)."""
     if C is None:
         C = torch.empty((t, W.n), dtype=torch.float32, device=a_qs.device)
     if ldc is None:
         ldc = C.shape[-1] if C.dim() > 1 else W.n
-    ws = W.struct()
+    _need_act(a_qs, a_sd, t, W.k, LAYOUT_PLANE64, "q8_gemm")
+    _need(C, "C", torch.float32, (t - 1) * ldc + W.n if t > 0 else 0)
+    ws = W.q8_struct() if isinstance(W, Q4KWeights) else W.struct()
     _check(lib().q8_gemm(ctypes.byref(ws), _ptr(a_qs), _ptr(a_sd), t, _ptr(C), ldc, _stream(a_qs.device)), "q8_gemm")
     return C
 
@@ -355,6 +468,11 @@ def q8_gemm_shared_multi(Ws: list[Q8Weights], a_qs: torch.Tensor, a_sd: torch.Te
         Cs = [torch.empty((t, W.n), dtype=torch.float32, device=a_qs.device) for W in Ws]
     if ldcs is None:
         ldcs = [C.shape[-1] if C.dim() > 1 else W.n for C, W in zip(Cs, Ws)]
+    if m == 0 or len(Cs) != m or len(ldcs) != m:
+        raise ValueError(f"{m} weight matrices, {len(Cs)} outputs, {len(ldcs)} leading dimensions")
+    _need_act(a_qs, a_sd, t, Ws[0].k, LAYOUT_PLANE64, "q8_gemm_shared_multi")
+    for i, (W, C, ld) in enumerate(zip(Ws, Cs, ldcs)):
+        _need(C, f"C[{i}]", torch.float32, (t - 1) * ld + W.n if t > 0 and W.n > 0 else 0)
     structs = [W.struct() for W in Ws]
     wps = (ctypes.POINTER(_Weights) * m)(*[ctypes.pointer(s) for s in structs])
     cps = (ctypes.c_void_p * m)(*[_ptr(C) for C in Cs])
@@ -362,3 +480,18 @@ def q8_gemm_shared_multi(Ws: list[Q8Weights], a_qs: torch.Tensor, a_sd: torch.Te
     _check(lib().q8_gemm_shared_multi(m, wps, _ptr(a_qs), _ptr(a_sd), t, cps, lds, _stream(a_qs.device)),
            "q8_gemm_shared_multi")
     return Cs
+
+
+# ---------------------------------------------------------------------------
+# Measurement helper
+# ---------------------------------------------------------------------------
+def hbm_read_probe(buf: torch.Tensor, workgroups: int, loads_per_lane: int = 1, out=None) -> torch.Tensor:
+    """One launch streaming every byte of buf once (the practical HBM read rate; see
+    q8_hbm_read_probe in include/q8proj.h). Returns the per-workgroup XOR words."""
+    if out is None:
+        out = torch.empty(workgroups, dtype=torch.int32, device=buf.device)
+    _need(out, "out", _I32, workgroups)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().q8_hbm_read_probe(_ptr(buf), nbytes, workgroups, loads_per_lane, _ptr(out), _stream(buf.device)),
+           "q8_hbm_read_probe")
+    return out

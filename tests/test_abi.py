@@ -41,7 +41,7 @@ def test_exports_every_declared_function(L):
     assert len(names) >= 12
     for n in names:
         assert hasattr(L, n), f"{n} declared in q8proj.h but not exported"
-    assert L.q8_abi_version() == 3
+    assert L.q8_abi_version() == 4
     assert L.q8_strerror(-3).decode().startswith("pointer not aligned")
 
 
@@ -50,6 +50,37 @@ def test_act_bytes_match_layouts(L, T, K):
     assert q8lib.act_bytes(T, K, q8lib.LAYOUT_ROW) == (T * K, T * K // 32 * 4)
     nq, ns = oracle.plane_sizes(T, K)
     assert q8lib.act_bytes(T, K, q8lib.LAYOUT_PLANE64) == (nq, ns * 4)
+
+
+@pytest.mark.parametrize("T,K", [(1, 32), (64, 3584), (3325, 3584), (3325, 18944), (65, 96)])
+def test_plane_bytes_is_the_plane64_act_bytes(L, T, K):
+    assert q8lib.plane_bytes(T, K) == q8lib.act_bytes(T, K, q8lib.LAYOUT_PLANE64)
+    nq, ns = oracle.plane_sizes(T, K)
+    assert q8lib.plane_bytes(T, K) == (nq, ns * 4)
+    q, sz = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.q8_plane_bytes(T, K + 1, ctypes.byref(q), ctypes.byref(sz)) == Q8_ESHAPE
+    assert L.q8_plane_bytes(T, K, None, ctypes.byref(sz)) == Q8_EINVAL
+
+
+def test_weight_format_is_checked_before_launch(L):
+    """q8_weights.format: every GEMV and the grouped GEMM take Q8_0 only; q8_gemm also takes
+    q4_K (then K must be a multiple of 256); unknown formats are refused."""
+    f = FAKE
+    L.q8_launch_counts_reset()
+    W4 = q8lib._Weights(8, 512, ctypes.c_void_p(f), None, q8lib.WEIGHTS_Q4_K)
+    Wbad = q8lib._Weights(8, 512, ctypes.c_void_p(f), ctypes.c_void_p(f), 7)
+    one = lambda W: (ctypes.POINTER(q8lib._Weights) * 1)(ctypes.pointer(W))  # noqa: E731
+    ys = (ctypes.c_void_p * 1)(f)
+    assert L.q8_gemv(ctypes.byref(W4), f, f, f, None) == Q8_EINVAL
+    assert L.q8_gemv_f32(ctypes.byref(W4), f, f, None) == Q8_EINVAL
+    assert L.q8_gemv_shared_multi(1, one(W4), f, f, ys, None) == Q8_EINVAL
+    assert L.q8_gemm_shared_multi(1, one(W4), f, f, 64, ys, (ctypes.c_int64 * 1)(8), None) == Q8_EINVAL
+    assert L.q8_gemm(ctypes.byref(Wbad), f, f, 64, f, 8, None) == Q8_EINVAL
+    W4k = q8lib._Weights(8, 288, ctypes.c_void_p(f), None, q8lib.WEIGHTS_Q4_K)  # not whole super-blocks
+    assert L.q8_gemm(ctypes.byref(W4k), f, f, 64, f, 8, None) == Q8_ESHAPE
+    assert L.q8_gemm(ctypes.byref(W4), f + 4, f, 64, f, 8, None) == Q8_EALIGN
+    assert L.q8_gemm(ctypes.byref(W4), f, f, 0, f, 8, None) == Q8_OK  # T = 0: nothing to do
+    assert all(v == 0 for v in q8lib.launch_counts().values())
 
 
 def test_act_bytes_rejects(L):

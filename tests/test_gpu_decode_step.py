@@ -5,9 +5,11 @@ consumers read; [P1] s3: a launch at decode costs more than its bytes).
 
 Bars:
 - every output (y, the q8_0 activation, each grouped output, the f32 part) is bit-identical to
-  rmsnorm_quant followed by q8_gemv_shared_multi_plus_f32, each of which the other GPU tests
-  pin to the oracle; y is also checked against the oracle's f64 RMSNorm (1e-5) and the
-  activation against the oracle's quantize of that reference;
+  rmsnorm_quant followed by q8_gemv_shared_multi_plus_f32;
+- against the oracle, directly: y within 1e-5 of the oracle's f64 RMSNorm; the activation
+  bit-exact with the oracle's quantize of the y the launch wrote; every grouped output within
+  1e-5 of norm of the oracle's GEMV on that activation, and the f32 part likewise on the
+  oracle's quantize of its own input;
 - consecutive calls on different rows each give their own row's results;
 - the one-launch form counts one launch; other shapes fall back to the two calls;
 - graph replays reproduce the eager results, with eager calls and synchronizations between.
@@ -17,7 +19,7 @@ import pytest
 
 import oracle
 import synth
-from _gpu import assert_rel, ensure_built, poisoned, to_np, up, weights
+from _gpu import assert_norm, assert_rel, check_row_exact, ensure_built, poisoned, to_np, up, weights
 
 pytestmark = pytest.mark.gpu
 
@@ -48,14 +50,17 @@ CASES = [
 ]
 
 
-def _weights_or_empty(n, K, stream):
-    W = weights(synth.normal((max(n, 1), K), stream=stream, std=0.02))[0]
+def _weights_or_empty(n, K, stream, planes=None):
+    W, wq, wd = weights(synth.normal((max(n, 1), K), stream=stream, std=0.02))
+    if planes is not None:
+        planes.append((wq[:n], wd[:n]))
     return W if n else W.rows(0, 0)
 
 
-def _inputs(Ns, K, Nx, Kx, base):
-    Ws = [_weights_or_empty(n, K, base + 7 * i) for i, n in enumerate(Ns)]
-    Wx = _weights_or_empty(Nx, Kx, base + 50) if Nx is not None else None
+def _inputs(Ns, K, Nx, Kx, base, planes=None):
+    """Device weights (and, into `planes`, the oracle's planes of every member, then Wx's)."""
+    Ws = [_weights_or_empty(n, K, base + 7 * i, planes) for i, n in enumerate(Ns)]
+    Wx = _weights_or_empty(Nx, Kx, base + 50, planes) if Nx is not None else None
     w = synth.normal((K,), stream=base + 51, mean=1.0, std=0.1)
     return Ws, Wx, w
 
@@ -97,13 +102,15 @@ def _assert_same(got, ref, what):
 
 @pytest.mark.parametrize("Ns,K,Nx,Kx,one", CASES)
 def test_step_bit_identical_to_two_calls(Ns, K, Nx, Kx, one):
-    Ws, Wx, wh = _inputs(Ns, K, Nx, Kx, 8100 + K + (Kx or 0))
+    planes = []
+    Ws, Wx, wh = _inputs(Ns, K, Nx, Kx, 8100 + K + (Kx or 0), planes)
     w = up(wh)
     o = Outs(K, Ws, Wx)
     # three different rows in a row: each call must read its own row's activation
     for r in range(3):
         xh = synth.normal((1, K), stream=8200 + 3 * K + r)
-        x, x2 = up(xh), (up(synth.normal((Kx,), stream=8300 + Kx + r)) if Kx else None)
+        x2h = synth.normal((Kx,), stream=8300 + Kx + r) if Kx else None
+        x, x2 = up(xh), (up(x2h) if Kx else None)
         ref = _reference(x, w, Ws, Wx, x2)
         torch.cuda.synchronize()
         q8lib.launch_counts_reset()
@@ -115,15 +122,20 @@ def test_step_bit_identical_to_two_calls(Ns, K, Nx, Kx, one):
         else:
             assert c.get(STEP, 0) == 0 and c["rmsnorm_quant"] == 1, c
         _assert_same(o.all(), [ref[0], ref[1], ref[2], *ref[3], ref[4]], f"{Ns}x{K} + {Nx}x{Kx}, row {r}")
-        if r == 0:  # the producer's output against the oracle
-            y_ref = oracle.rmsnorm_f64(xh, wh, EPS)
-            assert_rel(to_np(o.y), y_ref, 1e-5, f"rmsnorm 1x{K}")
-            q = to_np(o.aq).reshape(1, K)
-            d16, s = oracle.unpack_sd(to_np(o.asd).view(np.uint32).reshape(1, K // 32))
-            qo, do, _ = oracle.quantize(y_ref.astype(np.float32))
-            assert np.abs(q.astype(int) - qo.astype(int)).max() <= 1
-            assert np.abs(d16.astype(int) - do.astype(int)).max() <= 1
-            assert np.array_equal(s.astype(np.int64), q.reshape(1, -1, 32).astype(np.int64).sum(axis=2))
+        if r != 1:  # every output against the oracle (first and last row)
+            y_gpu = to_np(o.y).reshape(1, K)
+            assert_rel(y_gpu, oracle.rmsnorm_f64(xh, wh, EPS), 1e-5, f"rmsnorm 1x{K}")
+            check_row_exact(o.aq, o.asd, y_gpu, f"step activation 1x{K} vs the oracle's quantize of its y")
+            qa, da, _ = oracle.quantize(y_gpu)
+            for i, (n, out) in enumerate(zip(Ns, o.ys)):
+                wq, wd = planes[i]
+                ref, norm = oracle.gemv(wq, wd, qa[0], da[0])
+                assert_norm(to_np(out), ref, norm, 1e-5, f"step member {i} ({n}x{K}) vs the oracle")
+            if Nx:
+                wq, wd = planes[len(Ns)]
+                qx, dx, _ = oracle.quantize(x2h.reshape(1, -1))
+                ref, norm = oracle.gemv(wq, wd, qx[0], dx[0])
+                assert_norm(to_np(o.yx), ref, norm, 1e-5, f"step f32 part ({Nx}x{Kx}) vs the oracle")
 
 
 def test_step_without_f32_output():
@@ -185,3 +197,25 @@ def test_step_in_place_norm_runs_as_two_calls():
     c = {k: v for k, v in q8lib.launch_counts().items() if v}
     assert c.get(STEP, 0) == 0 and c["rmsnorm_quant"] == 1, c
     _assert_same([xin, o.aq, o.asd, *o.ys, o.yx], [ref[0], ref[1], ref[2], *ref[3], ref[4]], "in place")
+
+
+def test_step_row_with_overflowing_sum_of_squares():
+    """A row whose f32 sum of squares overflows takes the producer's rescaled second pass in
+    every workgroup of the one launch: the same bits as the two calls, and y within 1e-5 of the
+    oracle's f64 RMSNorm."""
+    Ns, K, Nx, Kx = [300, 200], 3584, 100, 256
+    planes = []
+    Ws, Wx, wh = _inputs(Ns, K, Nx, Kx, 8700, planes)
+    w = up(wh)
+    rng = np.random.default_rng(8701)
+    xh = (np.where(rng.integers(0, 2, K) == 0, -1.0, 1.0) * np.exp2(rng.uniform(60, 127, K))).astype(np.float32)
+    xh = xh.reshape(1, K)
+    x, x2 = up(xh), up(synth.normal((Kx,), stream=8702))
+    ref = _reference(x, w, Ws, Wx, x2)
+    o = Outs(K, Ws, Wx)
+    o.step(x, w, Ws, Wx, x2)
+    torch.cuda.synchronize()
+    _assert_same(o.all(), [ref[0], ref[1], ref[2], *ref[3], ref[4]], "overflowing row")
+    y_gpu = to_np(o.y).reshape(1, K)
+    assert_rel(y_gpu, oracle.rmsnorm_f64(xh, wh, EPS), 1e-5, "rmsnorm of an overflowing row", floor=2.0 ** -126)
+    check_row_exact(o.aq, o.asd, y_gpu, "activation of an overflowing row")

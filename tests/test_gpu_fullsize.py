@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 import synth
-from _gpu import assert_norm, assert_rel, ensure_built, plane_act, poisoned, row_act, to_np, up, weights
+from _gpu import (assert_norm, assert_rel, check_plane_exact, check_row_exact, ensure_built, plane_act,
+                  poisoned, row_act, to_np, up, weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +96,7 @@ def test_decode_projection_set_full():
     pys, py128 = q8lib.q8_gemv_shared_multi_plus_f32([ws[n][0] for n in names], aq, asd, W128, up(x128).view(-1))
     torch.cuda.synchronize()
     assert_rel(to_np(y), y_ref, 1e-5, "rmsnorm 1x7168")
+    check_row_exact(aq_f, asd_f, to_np(y), "rmsnorm_quant 1x7168 vs the oracle's quantize of its y")
     assert torch.equal(aq_f, aq2) and torch.equal(asd_f, asd2), "fused quantize differs from standalone"
     for n, out in zip(names, grouped):
         _, wq, wd = ws[n]
@@ -121,6 +123,7 @@ def test_prefill_rms_full():
     torch.cuda.synchronize()
     y_ref = oracle.rmsnorm_f64(x, w, EPS)
     assert_rel(to_np(y), y_ref, 1e-5, "rmsnorm 3325x3584")
+    check_plane_exact(pq_f, ps_f, to_np(y), "rmsnorm_quant 3325x3584 vs the oracle's quantize of its y")
     assert torch.equal(pq_f, pq2) and torch.equal(ps_f, ps2), "fused plane differs from standalone"
     del y, pq2, ps2
     pq, ps, qo, do, _ = plane_act(y_ref.astype(np.float32))
@@ -150,6 +153,7 @@ def test_prefill_swiglu_full():
     torch.cuda.synchronize()
     y_ref = oracle.swiglu_f64(g, u)
     assert_rel(to_np(y), y_ref, 1e-5, "swiglu 3325x18944")
+    check_plane_exact(pq_f, ps_f, to_np(y), "swiglu_quant 3325x18944 vs the oracle's quantize of its y")
     assert torch.equal(pq_f, pq2) and torch.equal(ps_f, ps2), "fused plane differs from standalone"
     del y, pq_f, ps_f, pq2, ps2, g, u
     torch.cuda.empty_cache()
@@ -166,7 +170,7 @@ def test_lm_head_full():
     x512 = synth.tensor(wl, "x512")
     W, wq, wd = workload_weights(wl, "W")
     y1, aq1, asd1 = q8lib.rmsnorm_quant(up(x1), up(w), EPS, ROW)
-    y512, _, _ = q8lib.rmsnorm_quant(up(x512), up(w), EPS, PLANE)
+    y512, pq512, ps512 = q8lib.rmsnorm_quant(up(x512), up(w), EPS, PLANE)
     r1 = oracle.rmsnorm_f64(x1, w, EPS)
     r512 = oracle.rmsnorm_f64(x512, w, EPS)
     aq, asd, qo1, do1, _ = row_act(r1.astype(np.float32))
@@ -183,6 +187,8 @@ def test_lm_head_full():
     assert torch.equal(s_logits.view(torch.int32), two.view(torch.int32)), "one-launch T=1 slice differs"
     assert_rel(to_np(y1), r1, 1e-5, "rmsnorm 1x3584")
     assert_rel(to_np(y512), r512, 1e-5, "rmsnorm 512x3584")
+    check_row_exact(aq1, asd1, to_np(y1), "rmsnorm_quant 1x3584 vs the oracle's quantize of its y")
+    check_plane_exact(pq512, ps512, to_np(y512), "rmsnorm_quant 512x3584 vs the oracle's quantize of its y")
     ref, norm = oracle.gemv(wq, wd, qo1[0], do1[0])
     assert_norm(to_np(logits), ref, norm, 1e-5, "lm head gemv 152064x3584")
     pq, ps, qo, do, _ = plane_act(r512.astype(np.float32))

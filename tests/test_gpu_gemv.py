@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from _gpu import assert_norm, ensure_built, poisoned, row_act, to_np, up, weights
+from _gpu import assert_norm, divide_blocks_f32, ensure_built, poisoned, row_act, to_np, up, weights
 
 pytestmark = pytest.mark.gpu
 
@@ -201,6 +201,30 @@ def test_gemv_f32_equals_quantize_then_gemv(N, K):
         qo, do, _ = oracle.quantize(x)
         ref, norm = oracle.gemv(wq, wd, qo[0], do[0])
         assert_norm(to_np(y), ref, norm, 1e-5, f"q8_gemv_f32 {N}x{K} vs oracle")
+
+
+@pytest.mark.parametrize("pad_to", [256, 2048])
+def test_gemv_f32_quantizes_with_ieee_division(pad_to):
+    """The one-lane quantize inside q8_gemv_f32 on blocks where the IEEE quotient x/d and a
+    reciprocal multiply round to different integers. The weights are the identity with unit
+    scales (qs = 1 on the diagonal, d = f16 1.0), so y[n] = f16(d_a) * q_a[n] exactly and every
+    activation value shows in the output: y must equal the oracle's quantize bit for bit."""
+    blocks = divide_blocks_f32().reshape(1, -1)
+    K = pad_to
+    x = np.zeros((1, K), np.float32)
+    x[0, : blocks.size] = blocks
+    x[0, blocks.size:] = synth.normal((1, K - blocks.size), stream=4650)[0]
+    wq = np.eye(K, dtype=np.int8)
+    wd = np.full((K, K // 32), 0x3C00, np.uint16)
+    W = q8lib.Q8Weights(up(wq), up(wd.view(np.int16)))
+    y = poisoned(K, torch.float32, 0xFF)
+    q8lib.q8_gemv_f32(W, up(x).view(-1), y)
+    torch.cuda.synchronize()
+    qo, do, _ = oracle.quantize(x)
+    exact = oracle.f16_to_f64(do[0])[np.arange(K) // 32] * qo[0].astype(np.float64)
+    assert np.array_equal(to_np(y).astype(np.float64), exact)
+    ref, norm = oracle.gemv(wq, wd, qo[0], do[0])
+    assert np.array_equal(ref, exact)
 
 
 # q8_gemv_shared_multi_plus_f32: (grouped member Ns, K) with (f32 part Nx, Kx), and the

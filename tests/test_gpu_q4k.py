@@ -96,3 +96,22 @@ def test_q4k_gemm_deterministic():
     b = run(W, pq, ps, T)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_q8_gemm_takes_q4k_weights_by_format():
+    """q8_gemm with a q8_weights descriptor of format Q8_WEIGHTS_Q4_K runs the q4_K GEMM: the
+    same bits as q4k_gemm, counted under q8_gemm, and the oracle's values."""
+    T, N, K = 130, 300, 1024
+    blocks = synth.q4k_blocks(N, K, 6400)
+    pq, ps, qo, do, so = plane_act(synth.normal((T, K), stream=6401))
+    W = dev_weights(blocks, K)
+    ref_c = run(W, pq, ps, T)
+    C = poisoned(T * N, torch.float32, 0xFF).view(T, N)
+    torch.cuda.synchronize()
+    q8lib.launch_counts_reset()
+    q8lib.q8_gemm(W, pq, ps, T, C)
+    torch.cuda.synchronize()
+    assert {k: v for k, v in q8lib.launch_counts().items() if v} == {"q8_gemm": 1}
+    assert torch.equal(C.view(torch.int32), ref_c.view(torch.int32))
+    ref, norm = oracle.q4k_gemm(blocks, N, K, qo, do, so)
+    assert_norm(to_np(C), ref, norm, 1e-5, "q8_gemm with q4_K weights")

@@ -171,6 +171,74 @@ def test_quantize_is_nearest_integer_on_exact_scale_grid():
         assert np.all(oracle.f16_to_f64(d16) == 2.0 ** k)
 
 
+def divide_blocks():
+    """(amax bits, x bits) of blocks [amax, x, 0, ...] on which the IEEE quotient and a
+    reciprocal multiply round to different integers (tests/golden/quantize_divide_blocks.json)."""
+    with open(os.path.join(GOLDEN, "quantize_divide_blocks.json")) as f:
+        return [(int(a, 16), int(b, 16)) for a, b in json.load(f)["blocks"]]
+
+
+DIVIDE_BLOCKS = divide_blocks()
+
+
+def _bits_f32(b: int) -> np.float32:
+    return np.array([b], dtype=np.uint32).view(np.float32)[0]
+
+
+def _round_f32(r):
+    """The binary32 value nearest to the rational r, ties to even, from the format's
+    definition: 24 significant bits at or above 2^-126, a fixed step of 2^-149 below
+    (the values here stay far from overflow)."""
+    from fractions import Fraction
+
+    if r == 0:
+        return Fraction(0)
+    a = abs(r)
+    e = a.numerator.bit_length() - a.denominator.bit_length()  # 2^e <= a < 2^(e+2)
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    step = Fraction(2) ** (max(e, -126) - 23)
+    m = round(a / step)  # Fraction.__round__ is half-even
+    return (m * step) if r > 0 else -(m * step)
+
+
+def _q_exact(amax_bits: int, x_bits: int):
+    """(q with the IEEE divide, q with a reciprocal multiply) for value x of a block whose
+    largest magnitude is amax: d = fl(amax/127), q = rint(fl(x/d)) ties to even, clamped."""
+    from fractions import Fraction
+
+    amax, x = Fraction(float(_bits_f32(amax_bits))), Fraction(float(_bits_f32(x_bits)))
+    d = _round_f32(amax / 127)
+    q_div = round(_round_f32(x / d))
+    q_rcp = round(_round_f32(x * _round_f32(1 / d)))
+    clamp = lambda q: max(-127, min(127, q))  # noqa: E731
+    return clamp(q_div), clamp(q_rcp), d
+
+
+def test_quantize_uses_ieee_division_not_reciprocal():
+    """The quantize divides (q = rint(x/d) with the correctly rounded f32 quotient), as the
+    activation-quantize definition states it; a multiply by the rounded reciprocal 1/d lands
+    one step away on every block below, so an oracle that multiplied would fail here."""
+    x = np.zeros((len(DIVIDE_BLOCKS), 32), np.float32)
+    for i, (a, b) in enumerate(DIVIDE_BLOCKS):
+        x[i, 0], x[i, 1] = _bits_f32(a), _bits_f32(b)
+        assert abs(x[i, 1]) <= x[i, 0]
+    qs, d16, ssum = oracle.quantize(x.reshape(1, -1))
+    qs = qs.reshape(len(DIVIDE_BLOCKS), 32)
+    for i, (a, b) in enumerate(DIVIDE_BLOCKS):
+        q_div, q_rcp, d = _q_exact(a, b)
+        assert q_div != q_rcp, "the block does not tell the two forms apart"
+        q_amax, _, _ = _q_exact(a, a)
+        assert q_amax == 127
+        assert int(qs[i, 1]) == q_div, f"block {i}: q {qs[i, 1]}, exact divide {q_div}, reciprocal {q_rcp}"
+        assert int(qs[i, 0]) == 127 and not qs[i, 2:].any()
+        assert int(ssum[0, i]) == 127 + q_div
+        # the stored scale is the f16 rounding of the same d
+        assert oracle.f16_to_f64(d16[0, i]) == float(np.float16(float(d)))
+
+
 # ---------------------------------------------------------------------------
 # Layouts
 # ---------------------------------------------------------------------------
