@@ -27,24 +27,29 @@ constexpr int kDppQuadXor2 = 0x4E;      // quad_perm:[2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i inside each 8 lanes
 constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i inside each 16 lanes
 
+// Lane permutations inside rows of 16 lanes. Every lane of these patterns reads
+// a lane of its own row, so no source is out of range; bound_ctrl then lets the
+// compiler fold the move into the instruction that consumes it
+// (v_add_f32_dpp, v_max_u32_dpp, ...), one instruction per step.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
-                                                                 __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
 // All-reduce over each aligned group of 8 lanes. After the two quad steps
 // every lane holds its quad's result; the half-mirror step pairs lane i with
 // lane 7-i, i.e. each quad with the other quad of its 8-lane group.
-__device__ __forceinline__ float max8(float a) {
-    a = fmaxf(a, dpp_f<kDppQuadXor1>(a));
-    a = fmaxf(a, dpp_f<kDppQuadXor2>(a));
-    a = fmaxf(a, dpp_f<kDppRowHalfMirror>(a));
+// umax8 takes the bit patterns of non-negative floats, whose unsigned order is
+// their numeric order (the integer max needs no NaN canonicalization).
+__device__ __forceinline__ uint32_t umax8(uint32_t a) {
+    a = max(a, (uint32_t)dpp_i<kDppQuadXor1>((int)a));
+    a = max(a, (uint32_t)dpp_i<kDppQuadXor2>((int)a));
+    a = max(a, (uint32_t)dpp_i<kDppRowHalfMirror>((int)a));
     return a;
 }
 
@@ -54,6 +59,28 @@ __device__ __forceinline__ int sum8(int s) {
     s += dpp_i<kDppRowHalfMirror>(s);
     return s;
 }
+
+__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// amax / 127 correctly rounded (the IEEE quotient) in three instructions:
+// q = amax * RN(1/127), then one fma correction of the remainder. Checked
+// against the IEEE division for every non-negative f32, subnormals included
+// (tests/test_quantize_arithmetic.py).
+__device__ __forceinline__ float div127(float a) {
+    constexpr float c = 1.0f / 127.0f;
+    const float q = a * c;
+    return fmaf(fmaf(-q, 127.0f, a), c, q);
+}
+
+// Half-integer margin of the reciprocal path: with |x/d| <= 128 and v_rcp_f32
+// within one ulp, |x/d - x*r| <= 2^-16, so a residual |x*r - rint(x*r)| below
+// 0.5 - 2^-14 puts x/d (and its f32 rounding) strictly inside the same integer's
+// rounding interval.
+constexpr float kHalfMargin = 0.5f - 0x1p-14f;
+
+// True when d is a nonzero f32-subnormal: the reciprocal bound above needs a normal d.
+__device__ __forceinline__ bool subnormal_nonzero(float d) { return fbits(d) - 1u < 0x007FFFFFu; }
 
 // Sum over all 64 lanes with a fixed tree; every lane receives the same bits.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -75,9 +102,6 @@ __device__ __forceinline__ float f16_value(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
 }
 
-// True when z is within 2^-14 of a half-integer (n = rint(z)).
-__device__ __forceinline__ bool near_half(float z, float n) { return fabsf(fabsf(z - n) - 0.5f) <= 0x1p-14f; }
-
 __device__ __forceinline__ int clamp127(float n) { return min(127, max(-127, (int)n)); }
 
 struct Quant8 {
@@ -85,26 +109,31 @@ struct Quant8 {
     uint32_t sd;   // f16 bits of d | (uint16)ssum << 16, identical in all 8 lanes
 };
 
+__device__ __forceinline__ uint32_t pack4(int q0, int q1, int q2, int q3) {
+    return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+           ((uint32_t)(q3 & 0xFF) << 24);
+}
+
 // The one quantize body of the library ([P2] section 3.2, phase 2): every
 // producer (q8_quantize, rmsnorm_quant, swiglu_quant) calls it on the f32
 // values it has just produced, so their quantized outputs are bit-identical
 // by construction. The 8 lanes of an aligned group hold one 32-value block.
 //
 // q = rint(x / d) with x/d the correctly rounded f32 quotient, computed
-// exactly but cheaply: z = x * rcp(d) is within 2^-15 of x/d for |x/d| <= 128
-// (v_rcp_f32 is within 1 ulp, plus two roundings), so rint(z) == rint(x/d)
-// unless z lies within 2^-14 of a half-integer; those lanes (and blocks with
-// an f32-subnormal d) redo the four values with the IEEE division.
+// exactly but cheaply: n = rint(x * r) with r = rcp(d) is that integer unless
+// the residual x*r - n comes within 2^-14 of a half (kHalfMargin); those
+// lanes, and blocks with a subnormal d, redo their four values with the IEEE
+// division. |x/d| <= 127 (+1 ulp) for a normal d, so the clamp only acts there.
 __device__ __forceinline__ Quant8 quantize_block8(float4 v) {
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    a = max8(a);  // exact in any order
-    const float d = a / 127.0f;
+    const uint32_t am = max(max(fbits(fabsf(v.x)), fbits(fabsf(v.y))), max(fbits(fabsf(v.z)), fbits(fabsf(v.w))));
+    const float a = bitsf(umax8(am));  // exact in any order
+    const float d = div127(a);
     const float r = d != 0.0f ? __builtin_amdgcn_rcpf(d) : 0.0f;  // d == 0: all q are 0
-    const float z0 = v.x * r, z1 = v.y * r, z2 = v.z * r, z3 = v.w * r;
-    float n0 = __builtin_rintf(z0), n1 = __builtin_rintf(z1), n2 = __builtin_rintf(z2), n3 = __builtin_rintf(z3);
-    const int slow = (int)(d != 0.0f && d < 0x1p-126f) | (int)near_half(z0, n0) | (int)near_half(z1, n1) |
-                     (int)near_half(z2, n2) | (int)near_half(z3, n3);
-    if (slow) {
+    float n0 = __builtin_rintf(v.x * r), n1 = __builtin_rintf(v.y * r), n2 = __builtin_rintf(v.z * r),
+          n3 = __builtin_rintf(v.w * r);
+    const float e = fmaxf(fmaxf(fabsf(fmaf(v.x, r, -n0)), fabsf(fmaf(v.y, r, -n1))),
+                          fmaxf(fabsf(fmaf(v.z, r, -n2)), fabsf(fmaf(v.w, r, -n3))));
+    if (e >= kHalfMargin || subnormal_nonzero(d)) {
         n0 = __builtin_rintf(v.x / d);
         n1 = __builtin_rintf(v.y / d);
         n2 = __builtin_rintf(v.z / d);
@@ -113,8 +142,7 @@ __device__ __forceinline__ Quant8 quantize_block8(float4 v) {
     const int q0 = clamp127(n0), q1 = clamp127(n1), q2 = clamp127(n2), q3 = clamp127(n3);
     const int s = sum8(q0 + q1 + q2 + q3);
     Quant8 res;
-    res.qs4 = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
-              ((uint32_t)(q3 & 0xFF) << 24);
+    res.qs4 = pack4(q0, q1, q2, q3);
     res.sd = f16_bits(d) | ((uint32_t)(uint16_t)(int16_t)s << 16);
     return res;
 }
@@ -124,25 +152,25 @@ __device__ __forceinline__ Quant8 quantize_block8(float4 v) {
 // is redone for all 32 values when any of them is near a half-integer; for the
 // others it gives the same integer as the reciprocal path. ssum is not formed.
 __device__ __forceinline__ void quantize_lane32(const float4 (&v)[8], uint4& q0, uint4& q1, uint32_t& dbits) {
-    float a = 0.0f;
+    uint32_t am = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        a = fmaxf(a, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
-    const float d = a / 127.0f;
+        am = max(am, max(max(fbits(fabsf(v[i].x)), fbits(fabsf(v[i].y))),
+                         max(fbits(fabsf(v[i].z)), fbits(fabsf(v[i].w)))));
+    const float d = div127(bitsf(am));
     const float r = d != 0.0f ? __builtin_amdgcn_rcpf(d) : 0.0f;
     float n[32];
-    int slow = (int)(d != 0.0f && d < 0x1p-126f);
+    float e = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float x4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const float z = x4[c] * r;
-            n[4 * i + c] = __builtin_rintf(z);
-            slow |= (int)near_half(z, n[4 * i + c]);
+            n[4 * i + c] = __builtin_rintf(x4[c] * r);
+            e = fmaxf(e, fabsf(fmaf(x4[c], r, -n[4 * i + c])));
         }
     }
-    if (slow) {
+    if (e >= kHalfMargin || subnormal_nonzero(d)) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             n[4 * i + 0] = __builtin_rintf(v[i].x / d);
@@ -154,8 +182,7 @@ __device__ __forceinline__ void quantize_lane32(const float4 (&v)[8], uint4& q0,
     uint32_t w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        w[i] = (uint32_t)(clamp127(n[4 * i]) & 0xFF) | ((uint32_t)(clamp127(n[4 * i + 1]) & 0xFF) << 8) |
-               ((uint32_t)(clamp127(n[4 * i + 2]) & 0xFF) << 16) | ((uint32_t)(clamp127(n[4 * i + 3]) & 0xFF) << 24);
+        w[i] = pack4(clamp127(n[4 * i]), clamp127(n[4 * i + 1]), clamp127(n[4 * i + 2]), clamp127(n[4 * i + 3]));
     q0 = make_uint4(w[0], w[1], w[2], w[3]);
     q1 = make_uint4(w[4], w[5], w[6], w[7]);
     dbits = f16_bits(d);
