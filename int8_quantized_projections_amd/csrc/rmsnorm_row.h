@@ -53,17 +53,12 @@ __device__ __forceinline__ void store_quant(const Quant8& r, int64_t t, int c, i
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm + quantize of the rows of logical workgroup `wg` (WAVES / WPR rows,
-// WPR waves per row). The row stays in registers (NV float4 per lane,
-// K <= 256*WPR*NV) between the sum of squares and the output, so x is read
-// once, and w is loaded in the same wave of loads. Lane i of the row
-// (i = 64*(wave % WPR) + lane) holds float4 index i + 64*WPR*k; 8 consecutive
-// lanes hold one 32-value block. The sum of squares, and so every output bit,
-// depends on K, WPR and NV only.
-// NV == 0: rows wider than the register budget; x is read twice (the second
-// read hits L2), with the same per-lane order of the sum of squares.
-// Every wave of the workgroup must call it (WPR > 1 combines the waves'
-// partial sums through LDS behind a barrier). qs and sd may point to LDS.
+// RMSNorm + quantize, the row arithmetic shared by every form of the producer
+// ([P2] s3.2: scale = rsqrt(mean(x^2) + eps), y = x * scale * w, then the
+// quantize of y). A row is spread over WPR waves of a workgroup of WAVES waves;
+// lane i of the row (i = 64*(wave % WPR) + lane) holds float4 index
+// i + 64*WPR*k, so 8 consecutive lanes hold one 32-value block. The sum of
+// squares, and so every output bit, depends on K, WPR and NV only.
 //
 // A row whose f32 sum of squares overflows (|x| above about 1.8e19 / sqrt(K))
 // takes a second pass over x * 2^-80, whose squares stay in range for any
@@ -72,6 +67,148 @@ __device__ __forceinline__ void store_quant(const Quant8& r, int64_t t, int c, i
 // pass's bits. Every wave of a workgroup takes the second reduction when any
 // of its rows needs it, so the barrier inside is reached by all of them.
 // ---------------------------------------------------------------------------
+constexpr float kDown = 0x1p-80f;  // the second pass's prescale
+
+// The row's total over its WPR waves, and (any_big) whether the total of any
+// row of the workgroup is not finite -- the same answer in every wave of the
+// workgroup. WPR > 1 combines the waves' partial sums in buf (WAVES floats of
+// LDS) behind a barrier that every wave of the workgroup must reach.
+template <int WPR, int WAVES>
+__device__ __forceinline__ float rms_row_total(float ss, float* buf, bool& any_big) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    ss = wave_sum(ss);
+    if constexpr (WPR > 1) {
+        constexpr int kRowsPerWg = WAVES / WPR;
+        if (lane == 0) buf[wave] = ss;
+        __syncthreads();
+        float mine = 0.0f;
+        bool any = false;
+#pragma unroll
+        for (int r = 0; r < kRowsPerWg; ++r) {
+            float tot = buf[r * WPR];
+#pragma unroll
+            for (int i = 1; i < WPR; ++i) tot += buf[r * WPR + i];
+            any |= !__builtin_isfinite(tot);
+            if (r == wave / WPR) mine = tot;
+        }
+        any_big = any;
+        return mine;
+    } else {
+        any_big = !__builtin_isfinite(ss);
+        return ss;
+    }
+}
+
+// The rest of the row once its share is in registers: v[k] holds x (float4
+// index li + 64*WPR*k of row t, any value past K or for a padded row), wv[k]
+// the same index of w. Writes y (unless NULL) and the quantized output of row
+// t. part, part2: WAVES floats of LDS each (the two passes' partial sums).
+// Every wave of the workgroup must call it.
+template <int D, int NV, int WPR, int WAVES>
+__device__ __forceinline__ void rms_finish(float4 (&v)[NV], const float4 (&wv)[NV], float eps,
+                                           float* __restrict__ y, int64_t t, int64_t rows, int64_t tpad, int K,
+                                           int nb, int8_t* __restrict__ qs, uint32_t* __restrict__ sd, float* part,
+                                           float* part2) {
+    constexpr int kStride = kWave * WPR;  // float4 stride between a lane's elements
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = (wave % WPR) * kWave + lane;  // lane index inside the row
+    const bool live = t < rows;
+    const bool inrow = t < tpad;  // uniform per wave
+    const int n4 = K >> 2;
+    // masks applied only after every load is in flight
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+        if (!live || li + kStride * k >= n4) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        ss = fmaf(v[k].x, v[k].x, ss);
+        ss = fmaf(v[k].y, v[k].y, ss);
+        ss = fmaf(v[k].z, v[k].z, ss);
+        ss = fmaf(v[k].w, v[k].w, ss);
+    }
+    bool any_big;
+    ss = rms_row_total<WPR, WAVES>(ss, part, any_big);
+    // [P2] s3.2: scale = rsqrt(ss/d + eps), y = x * scale * w.
+    float scale = rsqrtf(ss / (float)K + eps), pre = 1.0f;
+    if (any_big) {  // uniform over the workgroup
+        float s2 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const float a = v[k].x * kDown, b = v[k].y * kDown, c = v[k].z * kDown, d = v[k].w * kDown;
+            s2 = fmaf(a, a, s2);
+            s2 = fmaf(b, b, s2);
+            s2 = fmaf(c, c, s2);
+            s2 = fmaf(d, d, s2);
+        }
+        bool unused;
+        s2 = rms_row_total<WPR, WAVES>(s2, part2, unused);
+        if (!__builtin_isfinite(ss)) {
+            scale = rsqrtf(s2 / (float)K + eps * kDown * kDown);
+            pre = kDown;
+        }
+    }
+    if (!inrow) return;
+    // y == NULL: the quantized output only, no f32 row is written
+    float4* __restrict__ y4 = y != nullptr ? reinterpret_cast<float4*>(y + (live ? t : 0) * K) : nullptr;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int idx = li + kStride * k;
+        float4 o;  // pre is 1 (exact) unless the row took the second pass
+        o.x = v[k].x * pre * scale * wv[k].x;
+        o.y = v[k].y * pre * scale * wv[k].y;
+        o.z = v[k].z * pre * scale * wv[k].z;
+        o.w = v[k].w * pre * scale * wv[k].w;
+        if (y4 != nullptr && live && idx < n4) store_stream(reinterpret_cast<float*>(y4 + idx), o);
+        v[k] = o;  // zero for padded rows and past K
+    }
+    if constexpr (D != kDstNone) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int c = (li + kStride * k) >> 3;
+            if (c < nb) {
+                const Quant8 r = quantize_block8(v[k]);
+                store_quant<D>(r, t, c, (lane & 7) * 4, K, nb, qs, sd);
+            }
+        }
+    }
+}
+
+// Loads of row t's share (see rms_finish): x from clamped, always-valid
+// addresses (padded rows read row 0), w the same indices.
+template <int NV, int WPR>
+__device__ __forceinline__ void rms_load_x(float4 (&v)[NV], const float* __restrict__ x, int64_t t, int64_t rows,
+                                           int K) {
+    constexpr int kStride = kWave * WPR;
+    const int li = ((threadIdx.x >> 6) % WPR) * kWave + (threadIdx.x & 63);
+    const int n4 = K >> 2;
+    const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x + (t < rows ? t : 0) * K);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int idx = li + kStride * k;
+        v[k] = x4[idx < n4 ? idx : n4 - 1];
+    }
+}
+
+template <int NV, int WPR>
+__device__ __forceinline__ void rms_load_w(float4 (&wv)[NV], const float* __restrict__ w, int K) {
+    constexpr int kStride = kWave * WPR;
+    const int li = ((threadIdx.x >> 6) % WPR) * kWave + (threadIdx.x & 63);
+    const int n4 = K >> 2;
+    const float4* __restrict__ w4 = reinterpret_cast<const float4*>(w);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int idx = li + kStride * k;
+        wv[k] = w4[idx < n4 ? idx : n4 - 1];
+    }
+}
+
+// RMSNorm + quantize of the rows of logical workgroup `wg` (WAVES / WPR rows).
+// The row stays in registers (NV float4 per lane, K <= 256*WPR*NV) between the
+// sum of squares and the output, so x is read once, and w is loaded in the
+// same wave of loads. NV == 0: rows wider than the register budget; x is read
+// twice (the second read hits L2), with the same per-lane order of the sum of
+// squares. Every wave of the workgroup must call it. qs and sd may point to LDS.
 template <int D, int NV, int WPR, int WAVES>
 __device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const float* __restrict__ w, float eps,
                                              float* __restrict__ y, int64_t rows, int64_t tpad, int K, int nb,
@@ -83,107 +220,21 @@ __device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const 
     __shared__ float part2[WAVES];  // the rescaled second pass (a separate buffer: no wait for the first's readers)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = wg * kRowsPerWg + wave / WPR;
-    const int li = (wave % WPR) * kWave + lane;  // lane index inside the row
-    const bool live = t < rows;
-    const bool inrow = t < tpad;  // uniform per wave
-    const int n4 = K >> 2;
-    const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x + (live ? t : 0) * K);
-    const float4* __restrict__ w4 = reinterpret_cast<const float4*>(w);
-    // y == NULL: the quantized output only, no f32 row is written
-    float4* __restrict__ y4 = y != nullptr ? reinterpret_cast<float4*>(y + (live ? t : 0) * K) : nullptr;
-
-    // The row's total, and (any_big) whether the total of any row of the
-    // workgroup is not finite -- the same answer in every wave of the workgroup.
-    auto row_sum = [&](float ss, float* buf, bool& any_big) {
-        ss = wave_sum(ss);
-        if constexpr (WPR > 1) {
-            if (lane == 0) buf[wave] = ss;
-            __syncthreads();
-            float mine = 0.0f;
-            bool any = false;
-#pragma unroll
-            for (int r = 0; r < kRowsPerWg; ++r) {
-                float tot = buf[r * WPR];
-#pragma unroll
-                for (int i = 1; i < WPR; ++i) tot += buf[r * WPR + i];
-                any |= !__builtin_isfinite(tot);
-                if (r == wave / WPR) mine = tot;
-            }
-            any_big = any;
-            return mine;
-        } else {
-            any_big = !__builtin_isfinite(ss);
-            return ss;
-        }
-    };
-    constexpr float kDown = 0x1p-80f;  // the second pass's prescale
 
     if constexpr (NV > 0) {
         float4 v[NV], wv[NV];
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int idx = li + kStride * k;
-            const int ic = idx < n4 ? idx : n4 - 1;
-            v[k] = x4[ic];
-            wv[k] = w4[ic];
-        }
+        rms_load_x<NV, WPR>(v, x, t, rows, K);
+        rms_load_w<NV, WPR>(wv, w, K);
         __builtin_amdgcn_sched_barrier(0);  // keep every x and w load ahead of the math
-        // masks applied only after every load is in flight
-#pragma unroll
-        for (int k = 0; k < NV; ++k)
-            if (!live || li + kStride * k >= n4) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        float ss = 0.0f;
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            ss = fmaf(v[k].x, v[k].x, ss);
-            ss = fmaf(v[k].y, v[k].y, ss);
-            ss = fmaf(v[k].z, v[k].z, ss);
-            ss = fmaf(v[k].w, v[k].w, ss);
-        }
-        bool any_big;
-        ss = row_sum(ss, part, any_big);
-        // [P2] s3.2: scale = rsqrt(ss/d + eps), y = x * scale * w.
-        float scale = rsqrtf(ss / (float)K + eps), pre = 1.0f;
-        if (any_big) {  // uniform over the workgroup
-            float s2 = 0.0f;
-#pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const float a = v[k].x * kDown, b = v[k].y * kDown, c = v[k].z * kDown, d = v[k].w * kDown;
-                s2 = fmaf(a, a, s2);
-                s2 = fmaf(b, b, s2);
-                s2 = fmaf(c, c, s2);
-                s2 = fmaf(d, d, s2);
-            }
-            bool unused;
-            s2 = row_sum(s2, part2, unused);
-            if (!__builtin_isfinite(ss)) {
-                scale = rsqrtf(s2 / (float)K + eps * kDown * kDown);
-                pre = kDown;
-            }
-        }
-        if (!inrow) return;
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int idx = li + kStride * k;
-            float4 o;  // pre is 1 (exact) unless the row took the second pass
-            o.x = v[k].x * pre * scale * wv[k].x;
-            o.y = v[k].y * pre * scale * wv[k].y;
-            o.z = v[k].z * pre * scale * wv[k].z;
-            o.w = v[k].w * pre * scale * wv[k].w;
-            if (y4 != nullptr && live && idx < n4) store_stream(reinterpret_cast<float*>(y4 + idx), o);
-            v[k] = o;  // zero for padded rows and past K
-        }
-        if constexpr (D != kDstNone) {
-#pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const int c = (li + kStride * k) >> 3;
-                if (c < nb) {
-                    const Quant8 r = quantize_block8(v[k]);
-                    store_quant<D>(r, t, c, (lane & 7) * 4, K, nb, qs, sd);
-                }
-            }
-        }
+        rms_finish<D, NV, WPR, WAVES>(v, wv, eps, y, t, rows, tpad, K, nb, qs, sd, part, part2);
     } else {
+        const int li = (wave % WPR) * kWave + lane;  // lane index inside the row
+        const bool live = t < rows;
+        const bool inrow = t < tpad;  // uniform per wave
+        const int n4 = K >> 2;
+        const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x + (live ? t : 0) * K);
+        const float4* __restrict__ w4 = reinterpret_cast<const float4*>(w);
+        float4* __restrict__ y4 = y != nullptr ? reinterpret_cast<float4*>(y + (live ? t : 0) * K) : nullptr;
         float ss = 0.0f;
         if (live) {
             for (int idx = li; idx < n4; idx += kStride) {
@@ -195,7 +246,7 @@ __device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const 
             }
         }
         bool any_big;
-        ss = row_sum(ss, part, any_big);
+        ss = rms_row_total<WPR, WAVES>(ss, part, any_big);
         float scale = rsqrtf(ss / (float)K + eps), pre = 1.0f;
         if (any_big) {  // uniform over the workgroup
             float s2 = 0.0f;
@@ -210,7 +261,7 @@ __device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const 
                 }
             }
             bool unused;
-            s2 = row_sum(s2, part2, unused);
+            s2 = rms_row_total<WPR, WAVES>(s2, part2, unused);
             if (!__builtin_isfinite(ss)) {
                 scale = rsqrtf(s2 / (float)K + eps * kDown * kDown);
                 pre = kDown;
