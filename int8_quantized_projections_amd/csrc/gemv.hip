@@ -20,6 +20,7 @@
 //  - Per row: per-lane sums in block order, then a fixed butterfly over the
 //    W lanes. The order depends on K only, so 1, 2 or 4 rows per wave and the
 //    grouped launch give bit-identical outputs ([P1] s8 invariant).
+#include "gemm_common.h"
 #include "q8_common.h"
 #include "rmsnorm_row.h"
 
@@ -77,10 +78,16 @@ __device__ __forceinline__ int dot32(const uint4& w0, const uint4& w1, const uin
 // f32 (ax) and each lane quantizes the blocks it holds (one chunk only).
 // The GEMV of one wave: wave `wave_id` of `nwaves` takes row groups wave_id,
 // wave_id + nwaves, ...
-template <int W, int NBL, int R, bool MULTI, bool F32A, int KSEQ = 1>
+// PREF: pre_q, pre_d (LDS) hold the wave's first row group, already copied
+// there (one row, R == 1, W == 64, KSEQ == 1): for block column j, its two
+// 16-byte halves at pre_q + 2048j (+1024) + 16*lane, and its f16 scales at
+// pre_d, block b at byte 2b. The arithmetic is the same as from memory.
+template <int W, int NBL, int R, bool MULTI, bool F32A, int KSEQ = 1, bool PREF = false>
 __device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __restrict__ aq,
                                          const uint32_t* __restrict__ asd, const float* __restrict__ ax, int K,
-                                         int nb, int64_t groups, int64_t wave_id, int64_t nwaves) {
+                                         int nb, int64_t groups, int64_t wave_id, int64_t nwaves,
+                                         const int8_t* pre_q = nullptr, const uint16_t* pre_d = nullptr) {
+    static_assert(!PREF || (R == 1 && W == kWave && KSEQ == 1 && !F32A), "first row from LDS: one row, 64 lanes");
     constexpr int G = kWave / W;  // row slots per wave
     constexpr int CH = W * NBL;   // blocks per chunk
     constexpr int kSeq = KSEQ < NBL ? KSEQ : NBL;  // block columns per load step
@@ -168,6 +175,9 @@ __device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __r
             // waves then fall into fewer, denser address ranges. (A short grid, the
             // grouped x4 at 2.25 rows per wave, is the exception: 16.1 -> 17.6 us.)
             // The per-row order of the accumulation is unchanged (j ascending).
+            // the first row group from the LDS copy made during the producer
+            constexpr bool from_lds = PREF && decltype(first)::value;
+            if constexpr (from_lds) q8gemm::wait_copies();  // this wave's own copies have landed
 #pragma unroll
             for (int j0 = 0; j0 < NBL; j0 += kSeq) {
                 uint4 w0[R][kSeq], w1[R][kSeq];
@@ -178,9 +188,15 @@ __device__ __forceinline__ void gemv_run(const GemvArgs& args, const int8_t* __r
                     for (int jj = 0; jj < kSeq; ++jj) {
                         const int b = ch * CH + u + (j0 + jj) * W;
                         const int bc = b < nb ? b : nb - 1;
-                        w0[r][jj] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK);
-                        w1[r][jj] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK + 16);
-                        dw[r][jj] = drow[r][bc];
+                        if constexpr (from_lds) {
+                            w0[r][jj] = *reinterpret_cast<const uint4*>(pre_q + (j0 + jj) * 2048 + 16 * lane);
+                            w1[r][jj] = *reinterpret_cast<const uint4*>(pre_q + (j0 + jj) * 2048 + 1024 + 16 * lane);
+                            dw[r][jj] = pre_d[bc];
+                        } else {
+                            w0[r][jj] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK);
+                            w1[r][jj] = *reinterpret_cast<const uint4*>(wrow[r] + (int64_t)bc * kQK + 16);
+                            dw[r][jj] = drow[r][bc];
+                        }
                     }
                 }
                 if constexpr (F32A && decltype(first)::value) {
@@ -275,13 +291,22 @@ __global__ __launch_bounds__(256) void k_gemv_pair(GemvArgs a1, const int8_t* __
 constexpr int kStepWaves = 16;    // waves per workgroup of the decode step
 constexpr int kMaxStepK = 8192;   // the grouped part's K: one chunk of 64 lanes x 4 blocks
 
-template <int NV, int NBL, int R, int W2>
+//
+// PRE: every grouped wave copies its first row (weights and scales) into LDS
+// with direct buffer -> LDS copies issued right after the producer's x and w
+// loads, so the weight stream starts while the producer computes (a fixed
+// number of copies per wave: the producer then waits for its own loads only).
+// Needs K/32 even and 4-byte aligned scale rows (4-byte scale copies).
+template <int NV, int NBL, int R, int W2, bool PRE>
 __global__ __launch_bounds__(kStepWaves * 64) void k_decode_step(
     const float* __restrict__ xn, const float* __restrict__ wn, float eps, float* __restrict__ yn,
     int8_t* __restrict__ aq_out, uint32_t* __restrict__ asd_out, GemvArgs a1, int K1, int nb1, int64_t groups1,
     GemvArgs a2, const float* __restrict__ x2, int K2, int nb2, int64_t groups2, int wgs2) {
     __shared__ __attribute__((aligned(16))) int8_t act_q[kMaxStepK];
     __shared__ uint32_t act_sd[kMaxStepK / kQK];
+    __shared__ __attribute__((aligned(16))) int8_t pre_q[PRE ? kStepWaves * NBL * 2048 : 16];
+    __shared__ __attribute__((aligned(16))) uint32_t pre_d[PRE ? kStepWaves * 128 : 4];
+    __shared__ float part[kStepWaves], part2[kStepWaves];
     const int w = threadIdx.x >> 6;
     const int b = (int)blockIdx.x;
     if (b < wgs2) {
@@ -290,17 +315,55 @@ __global__ __launch_bounds__(kStepWaves * 64) void k_decode_step(
         return;
     }
     const bool writer = b == wgs2;
-    rmsnorm_rows<kDstRow, NV, kStepWaves, kStepWaves>(xn, wn, eps, writer ? yn : nullptr, 1, 1, K1, nb1, act_q,
-                                                      act_sd, 0);
-    __syncthreads();
+    // wave-uniform (scalar registers): the first row's member lookup below is scalar selects
+    const int64_t wave_id = (int64_t)(b - wgs2) * kStepWaves + __builtin_amdgcn_readfirstlane(w);
+    // the producer's loads first (they return in order), then the first-row copies
+    float4 xv[NV], wv[NV];
+    rms_load_x<NV, kStepWaves>(xv, xn, 0, 1, K1);
+    rms_load_w<NV, kStepWaves>(wv, wn, K1);
+    if constexpr (PRE) {
+        const int lane = threadIdx.x & 63;
+        // this wave's first row (row group wave_id, one row per group), as gemv_run finds it
+        const int64_t row = wave_id;
+        const bool valid = row < a1.total;
+        const int8_t* q = a1.wq[0];
+        const uint16_t* d = a1.wd[0];
+        int64_t o = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxMats; ++i) {
+            const bool in = row >= a1.off[i];
+            q = in ? a1.wq[i] : q;
+            d = in ? a1.wd[i] : d;
+            o = in ? a1.off[i] : o;
+        }
+        const int8_t* wrow = valid ? q + (row - o) * K1 : a1.safe_q;
+        const uint16_t* drow = valid ? d + (row - o) * nb1 : a1.safe_d;
+        const __amdgpu_buffer_rsrc_t rq = q8gemm::make_rsrc(wrow, K1);
+        const __amdgpu_buffer_rsrc_t rd = q8gemm::make_rsrc(drow, (int64_t)nb1 * 2);
+        int8_t* mq = pre_q + w * (NBL * 2048);
+#pragma unroll
+        for (int j = 0; j < NBL; ++j) {
+            const int bl = lane + 64 * j;
+            const uint32_t off = (uint32_t)((bl < nb1 ? bl : nb1 - 1) * kQK);
+            q8gemm::lds_copy16(rq, off, 0u, mq + j * 2048);
+            q8gemm::lds_copy16(rq, off + 16u, 0u, mq + j * 2048 + 1024);
+        }
+        q8gemm::lds_copy4(rd, (uint32_t)(4 * lane), 0u, &pre_d[w * 128]);
+        q8gemm::lds_copy4(rd, (uint32_t)(4 * lane + 256), 0u, &pre_d[w * 128 + 64]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load and copy issued ahead of the math
+    rms_finish<kDstRow, NV, kStepWaves, kStepWaves>(xv, wv, eps, writer ? yn : nullptr, 0, 1, 1, K1, nb1, act_q,
+                                                    act_sd, part, part2);
+    lds_barrier();  // the activation in LDS is complete; the first-row copies stay in flight
     if (writer) {
         for (int i = (int)threadIdx.x; i < K1 / 16; i += kStepWaves * 64)
             reinterpret_cast<uint4*>(aq_out)[i] = reinterpret_cast<const uint4*>(act_q)[i];
         for (int i = (int)threadIdx.x; i < nb1; i += kStepWaves * 64) asd_out[i] = act_sd[i];
     }
-    gemv_run<64, NBL, R, true, false>(a1, act_q, act_sd, nullptr, K1, nb1, groups1,
-                                      (int64_t)(b - wgs2) * kStepWaves + w,
-                                      (int64_t)((int)gridDim.x - wgs2) * kStepWaves);
+    gemv_run<64, NBL, R, true, false, 1, PRE>(a1, act_q, act_sd, nullptr, K1, nb1, groups1, wave_id,
+                                      (int64_t)((int)gridDim.x - wgs2) * kStepWaves,
+                                      PRE ? pre_q + w * (NBL * 2048) : nullptr,
+                                      PRE ? reinterpret_cast<const uint16_t*>(&pre_d[w * 128]) : nullptr);
 }
 
 struct Plan {
@@ -616,8 +679,16 @@ void launch_step3(const GemvJob& j1, const GemvJob& j2, hipStream_t s, const flo
         if (wgs2 > 0) wgs2 = slots - wgs1;
     }
     const dim3 grid((unsigned)(wgs2 + wgs1));
-    q8h::launch_kernel((k_decode_step<NV, NBL, 1, W2>), grid, dim3(kStepWaves * 64), 0, s, x, w, eps, y, a_qs, a_sd,
-                       j1.a, j1.K, j1.nb, j1.p.groups, j2.a, x2, j2.K, j2.nb, j2.p.groups, (int)wgs2);
+    // the first-row copies need 4-byte scale copies: K/32 even and 4-byte aligned scale planes
+    bool pre = j1.nb % 2 == 0;
+    for (int i = 0; i < kMaxMats; ++i)
+        if (j1.a.wd[i] != nullptr && !q8h::aligned(j1.a.wd[i], 4)) pre = false;
+    if (pre)
+        q8h::launch_kernel((k_decode_step<NV, NBL, 1, W2, true>), grid, dim3(kStepWaves * 64), 0, s, x, w, eps, y,
+                           a_qs, a_sd, j1.a, j1.K, j1.nb, j1.p.groups, j2.a, x2, j2.K, j2.nb, j2.p.groups, (int)wgs2);
+    else
+        q8h::launch_kernel((k_decode_step<NV, NBL, 1, W2, false>), grid, dim3(kStepWaves * 64), 0, s, x, w, eps, y,
+                           a_qs, a_sd, j1.a, j1.K, j1.nb, j1.p.groups, j2.a, x2, j2.K, j2.nb, j2.p.groups, (int)wgs2);
 }
 
 template <int NV, int NBL>

@@ -188,6 +188,13 @@ __device__ __forceinline__ void quantize_lane32(const float4 (&v)[8], uint4& q0,
     dbits = f16_bits(d);
 }
 
+// Workgroup barrier for data exchanged through LDS by ordinary LDS stores:
+// waits for this wave's LDS operations (lgkmcnt) but not for its global loads
+// or its global -> LDS copies (vmcnt), which __syncthreads() would also wait
+// for through its release fence. The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Workgroups are dealt to the 8 XCDs in turn (workgroup p runs on XCD p % 8).
 // Remap a linear workgroup index so that each XCD gets one contiguous range
 // of logical indices (the first count % 8 XCDs one more than the others):

@@ -80,7 +80,7 @@ __device__ __forceinline__ float rms_row_total(float ss, float* buf, bool& any_b
     if constexpr (WPR > 1) {
         constexpr int kRowsPerWg = WAVES / WPR;
         if (lane == 0) buf[wave] = ss;
-        __syncthreads();
+        lds_barrier();  // global loads and copies into LDS stay in flight
         float mine = 0.0f;
         bool any = false;
 #pragma unroll
