@@ -394,9 +394,68 @@ def gemm_entry(t, T, N, K):
             "min_bytes": mb, "GBps_min_bytes": mb / t["mean_us"] / 1e3}
 
 
-def hbm_entry(t, b, warm=None):
-    """A bandwidth-bound kernel's rate; warm: the same kernel on one set of buffers."""
+class Practical:
+    """Practical HBM ceilings of plain streams (q8_hbm_stream_probe) with a kernel's read/write mix
+    and total bytes, cold: regions of a 4 GiB pool rotate so that no launch finds its bytes in a
+    cache. The pattern is the one whose share of written bytes is nearest the kernel's: read-only
+    (0), two reads per write (1/3) or a copy (1/2)."""
+    GRID = (1024, 2048)
+
+    def __init__(self, D):
+        self.D = D
+        self.pool = None
+        self.out = None
+        self.cache = {}
+
+    @staticmethod
+    def pattern(read_b, write_b):
+        f = write_b / (read_b + write_b)
+        return min((("read", 0.0), ("2read_1write", 1 / 3), ("copy", 0.5)), key=lambda p: abs(p[1] - f))[0]
+
+    def ceiling(self, read_b, write_b):
+        torch, q8 = self.D.torch, self.D.q8
+        pat = self.pattern(read_b, write_b)
+        nstreams = {"read": 1, "2read_1write": 3, "copy": 2}[pat]
+        stream_b = int((read_b + write_b) / nstreams) // 4096 * 4096
+        key = (pat, stream_b >> 20)
+        if key in self.cache:
+            return self.cache[key]
+        if self.pool is None:
+            self.pool = torch.empty(4 << 30, dtype=torch.uint8, device=self.D.dev)
+            self.out = torch.empty(65536, dtype=torch.int32, device=self.D.dev)
+        set_b = stream_b * nstreams
+        nsets = max(2, min(math.ceil(COLD_BYTES / set_b), (4 << 30) // set_b))
+        bufs = [[self.pool[k * set_b + j * stream_b:k * set_b + (j + 1) * stream_b] for j in range(nstreams)]
+                for k in range(nsets)]
+        best = None
+        for wgs in self.GRID:
+            def one(i, wgs=wgs):
+                b = bufs[i % nsets]
+                if pat == "read":
+                    q8.hbm_stream_probe(stream_b, wgs, src0=b[0], out=self.out)
+                elif pat == "copy":
+                    q8.hbm_stream_probe(stream_b, wgs, src0=b[0], dst=b[1])
+                else:
+                    q8.hbm_stream_probe(stream_b, wgs, src0=b[0], src1=b[1], dst=b[2])
+            t = stats(time_each(self.D, one, 10))
+            gbs = set_b / t["mean_us"] / 1e3
+            if best is None or gbs > best["GBps"]:
+                best = {"pattern": pat, "bytes": set_b, "GBps": gbs, "mean_us": t["mean_us"], "workgroups": wgs}
+        self.cache[key] = best
+        return best
+
+
+PRACTICAL = None  # set in main()
+
+
+def hbm_entry(t, b, warm=None, read_b=None):
+    """A bandwidth-bound kernel's rate; warm: the same kernel on one set of buffers. read_b: the
+    bytes it reads (the rest are written), for the practical ceiling of that mix."""
     e = {**t, "bytes": b, "GBps": b / t["mean_us"] / 1e3, "frac_hbm": b / t["mean_us"] / 1e3 / HBM_PEAK_GBS}
+    if read_b is not None and PRACTICAL is not None:
+        c = PRACTICAL.ceiling(read_b, b - read_b)
+        e["practical"] = c
+        e["frac_of_practical"] = e["GBps"] / c["GBps"]
     if warm is not None:
         e["warm"] = {"mean_us": warm["mean_us"], "median_us": warm["median_us"],
                      "GBps": b / warm["mean_us"] / 1e3, "frac_hbm": b / warm["mean_us"] / 1e3 / HBM_PEAK_GBS,
@@ -442,7 +501,7 @@ def bench_prefill_rms(D, reps):
 
     t = stats(time_each(D, rms, reps))
     tw = stats(time_each(D, lambda i: rms(0), reps))
-    out["rmsnorm_quant_plane64"] = hbm_entry(t, b, tw)
+    out["rmsnorm_quant_plane64"] = hbm_entry(t, b, tw, read_b=T * K * 4 + K * 4)
     out["rmsnorm_quant_plane64"]["sets"] = ns
     prod_us = t["mean_us"]
     for i in range(ns):
@@ -504,11 +563,11 @@ def bench_prefill_swiglu(D, reps):
         q8.swiglu_quant(gi, ui, q8.LAYOUT_PLANE64, yi if f32 else None, qi, si, f32=f32)
 
     t = stats(time_each(D, sw, reps))
-    out["swiglu_quant_plane64"] = hbm_entry(t, b, stats(time_each(D, lambda i: sw(0), reps)))
+    out["swiglu_quant_plane64"] = hbm_entry(t, b, stats(time_each(D, lambda i: sw(0), reps)), read_b=T * K * 8)
     # plane only (y = NULL): for a down projection that reads no f32 activation
     t3 = stats(time_each(D, lambda i: sw(i, False), reps))
     b3 = b - T * K * 4
-    out["swiglu_quant_plane64_no_f32"] = hbm_entry(t3, b3)
+    out["swiglu_quant_plane64_no_f32"] = hbm_entry(t3, b3, read_b=T * K * 8)
     # the unfused form's quantize pass: q8_quantize of the f32 y into the same plane (bit-identical
     # to the fused plane), the activation quantize at bandwidth scale; 323 MB per set, 4 sets
     sw(0)
@@ -522,7 +581,7 @@ def bench_prefill_swiglu(D, reps):
         q8.q8_quantize(ysets[i % nq], q8.LAYOUT_PLANE64, *qsets[i % nq])
 
     t4 = stats(time_each(D, quant, reps))
-    out["q8_quantize_plane64"] = hbm_entry(t4, b4, stats(time_each(D, lambda i: quant(0), reps)))
+    out["q8_quantize_plane64"] = hbm_entry(t4, b4, stats(time_each(D, lambda i: quant(0), reps)), read_b=T * K * 4)
     del ysets[2:], qsets[2:]
     # the down GEMM: distinct (weights, plane, output) sets over >= 1 GB
     gb = gemm_min_bytes(T, N, K)
@@ -596,8 +655,7 @@ def bench_lm_head(D, reps):
     out["rmsnorm_quant_row_3584"] = {**t, "bytes": rms_bytes(1, K), "GBps": rms_bytes(1, K) / t["mean_us"] / 1e3}
     tg = stats(time_each(D, lambda i: q8.q8_gemv(Ws[i % n], aq, asd, logits), reps))
     gb = gemv_bytes(N, K)
-    out[f"q8_gemv_{N}x{K}"] = {**tg, "bytes": gb, "GBps": gb / tg["mean_us"] / 1e3,
-                                "frac_hbm": gb / tg["mean_us"] / 1e3 / HBM_PEAK_GBS}
+    out[f"q8_gemv_{N}x{K}"] = hbm_entry(tg, gb, read_b=gb - N * 4)
     out["t1_slice_tok_per_s_two_launches"] = 1.0 / ((t["mean_us"] + tg["mean_us"]) * 1e-6)
 
     # the T=1 slice in one launch: the output norm and the LM-head GEMV
@@ -732,12 +790,22 @@ def hbm_reference(D, mib=2048, reps=5):
     best = max(sweep, key=lambda k: sweep[k]["GBps"])
     dst = torch.empty_like(src)
     tc = stats(time_each(D, lambda i: dst.copy_(src), reps))
+    # the stream probe (q8_hbm_stream_probe) on the same buffers: writes only, and one read per write
+    nb = n * 4
+    tw = min((stats(time_each(D, lambda i, w=w: q8.hbm_stream_probe(nb, w, dst=dst), reps)) for w in Practical.GRID),
+             key=lambda t: t["mean_us"])
+    tp = min((stats(time_each(D, lambda i, w=w: q8.hbm_stream_probe(nb, w, src0=src, dst=dst), reps))
+              for w in Practical.GRID), key=lambda t: t["mean_us"])
     out = {"read_GBps": sweep[best]["GBps"], "read_bytes": n * 4, "read_launch": best,
            "read_kernel": "q8_hbm_read_probe (k_read_probe): 16-byte grid-stride loads, one pass, "
                           "workgroups x loads per lane in flight",
            "read_sweep": sweep, "frac_of_peak": sweep[best]["GBps"] / HBM_PEAK_GBS,
            "copy_bytes": 2 * n * 4, "copy_GBps": 2 * n * 4 / tc["mean_us"] / 1e3,
-           "copy_kernel": "torch copy_ of a %d MiB f32 buffer" % mib}
+           "copy_kernel": "torch copy_ of a %d MiB f32 buffer" % mib,
+           "write_GBps": nb / tw["mean_us"] / 1e3, "copy_probe_GBps": 2 * nb / tp["mean_us"] / 1e3,
+           "write_kernel": "q8_hbm_stream_probe (k_stream_probe) with a destination only / one source "
+                           "and one destination, 16-byte grid-stride, the better of %s workgroups"
+                           % "/".join(map(str, Practical.GRID))}
     del src, dst, out_words
     torch.cuda.empty_cache()
     return out
@@ -806,6 +874,8 @@ def main():
     which = set(["decode", "gemv2048", "prefill_rms", "prefill_swiglu", "lm_head", "prefill_q4k"]) \
         if args.configs == "all" \
         else set(args.configs.split(","))
+    global PRACTICAL
+    PRACTICAL = Practical(D)
     if "decode" not in which:  # profiling a subset: no headline line
         for name, fn in (("gemv2048", bench_gemv2048), ("prefill_rms", bench_prefill_rms),
                          ("prefill_swiglu", bench_prefill_swiglu), ("lm_head", bench_lm_head),
@@ -832,10 +902,15 @@ def main():
     # average launch duration: HIP events around a batch of back-to-back launches on the
     # launch stream (weights rotate over cold copies); per-launch event pairs are in components
     achieved = dom["bytes"] / (dom["batch_mean_us"] * 1e-6) / 1e9
+    practical = PRACTICAL.ceiling(dom["bytes"], 0)
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(dom_name),
                 "algorithmic_bytes": dom["bytes"], "mean_launch_us": dom["batch_mean_us"],
-                "launches_timed": 4 * args.reps}
+                "launches_timed": 4 * args.reps,
+                "practical": practical, "frac_of_practical": achieved / practical["GBps"]}
+    hbm["practical_ceilings"] = sorted(PRACTICAL.cache.values(), key=lambda c: (c["pattern"], c["bytes"]))
+    PRACTICAL.pool = None
+    torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu:
         log("[cpu] timing the oracle")

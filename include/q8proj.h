@@ -367,6 +367,22 @@ int q8_weights_repack(const void* gguf_blocks, int64_t n, int64_t k, int8_t* qs,
 int q8_hbm_read_probe(const void* buf, int64_t bytes, int workgroups, int loads_per_lane, uint32_t* out,
                       void* stream);
 
+/*
+ * Measurement helper, not part of the projection path: a plain stream of a
+ * given read/write mix, the practical ceiling of a producer with that mix. One
+ * launch reads `bytes` (a multiple of 16) from src0 and, when not NULL, from
+ * src1, and writes `bytes` to dst when dst is not NULL (the XOR of the sources,
+ * or a counter pattern with no source), over `workgroups` workgroups of 256
+ * lanes (1..65536), 16-byte grid-stride words. With dst NULL, workgroup i
+ * writes an XOR of what it read to out[i] (`workgroups` words; out is not used
+ * otherwise). Device buffers, 16-byte aligned (out 4-byte). src1 without
+ * src0, no source and no destination, or neither dst nor out: Q8_EINVAL; bytes
+ * not a multiple of 16 or workgroups outside 1..65536: Q8_ESHAPE. Not counted
+ * by the launch counters.
+ */
+int q8_hbm_stream_probe(const void* src0, const void* src1, void* dst, int64_t bytes, int workgroups, uint32_t* out,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

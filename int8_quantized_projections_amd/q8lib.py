@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "rmsnorm_quant_gemv_shared_multi_plus_f32": ([vp, vp, ctypes.c_float, vp, vp, vp, ci, ctypes.POINTER(wp),
                                                           ctypes.POINTER(vp), wp, vp, vp, vp], ci),
             "q8_hbm_read_probe": ([vp, i64, ci, ci, vp, vp], ci),
+            "q8_hbm_stream_probe": ([vp, vp, vp, i64, ci, vp, vp], ci),
             "q8_launch_counts": ([ctypes.POINTER(i64), ci], ci),
             "q8_launch_counts_reset": ([], None),
             "q8_launch_counter_name": ([ci], ctypes.c_char_p),
@@ -495,3 +496,18 @@ def hbm_read_probe(buf: torch.Tensor, workgroups: int, loads_per_lane: int = 1, 
     _check(lib().q8_hbm_read_probe(_ptr(buf), nbytes, workgroups, loads_per_lane, _ptr(out), _stream(buf.device)),
            "q8_hbm_read_probe")
     return out
+
+
+def hbm_stream_probe(nbytes: int, workgroups: int, src0=None, src1=None, dst=None, out=None) -> None:
+    """One launch of a plain stream: read nbytes from src0 (and src1), write nbytes to dst (see
+    q8_hbm_stream_probe in include/q8proj.h). Every given tensor must hold at least nbytes."""
+    for name, t in (("src0", src0), ("src1", src1), ("dst", dst)):
+        if t is not None and t.numel() * t.element_size() < nbytes:
+            raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, at least {nbytes} needed")
+    if dst is None and out is None:
+        raise ValueError("a read-only stream needs out (one int32 per workgroup)")
+    if out is not None:
+        _need(out, "out", _I32, workgroups)
+    dev = next(t for t in (src0, src1, dst) if t is not None).device
+    _check(lib().q8_hbm_stream_probe(_ptr(src0), _ptr(src1), _ptr(dst), nbytes, workgroups, _ptr(out), _stream(dev)),
+           "q8_hbm_stream_probe")

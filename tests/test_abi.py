@@ -330,3 +330,25 @@ def test_decode_step_rejects_before_launch(L):
     two = (ctypes.POINTER(q8lib._Weights) * 2)(ctypes.pointer(W), ctypes.pointer(W96))
     assert call(m=2, W=two, Y=(ctypes.c_void_p * 2)(f, f)) == Q8_ESHAPE  # grouped members share K
     assert all(v == 0 for v in q8lib.launch_counts().values())
+
+
+def test_probe_argument_checks(L):
+    """The measurement probes reject bad calls before launching anything."""
+    vp, u32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32)
+    rd = L.q8_hbm_read_probe
+    st = L.q8_hbm_stream_probe
+    fake = vp(FAKE)
+    out = ctypes.cast(FAKE, u32p)
+    assert rd(None, 1024, 64, 1, out, None) == Q8_EINVAL
+    assert rd(fake, 1024, 64, 3, out, None) == Q8_EINVAL
+    assert rd(fake, 1000, 64, 1, out, None) == Q8_ESHAPE
+    assert rd(fake, 1024, 0, 1, out, None) == Q8_ESHAPE
+    assert rd(vp(FAKE + 8), 1024, 64, 1, out, None) == Q8_EALIGN
+    assert rd(fake, 0, 64, 1, out, None) == Q8_OK
+    assert st(None, None, None, 1024, 64, out, None) == Q8_EINVAL      # nothing to stream
+    assert st(None, fake, fake, 1024, 64, None, None) == Q8_EINVAL     # src1 without src0
+    assert st(fake, None, None, 1024, 64, None, None) == Q8_EINVAL     # read only, no out
+    assert st(fake, None, fake, 1000, 64, None, None) == Q8_ESHAPE
+    assert st(fake, None, fake, 1024, 65537, None, None) == Q8_ESHAPE
+    assert st(fake, None, vp(FAKE + 4), 1024, 64, None, None) == Q8_EALIGN
+    assert st(fake, None, fake, 0, 64, None, None) == Q8_OK
