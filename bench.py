@@ -180,6 +180,17 @@ def time_batch(D, fn, reps, warm=3):
     return a.elapsed_time(b) / reps
 
 
+def timed(D, fn, reps):
+    """Device time per launch of fn(i). mean_us: the mean over a back-to-back batch of 4*reps
+    launches with one pair of HIP events around the batch, the kernel's own duration as a trace
+    shows it; each: the per-launch event pairs, where every interval also holds that launch's
+    dispatch (a few microseconds, the whole time of a tiny kernel)."""
+    each = stats(time_each(D, fn, reps))
+    batch_us = time_batch(D, fn, 4 * reps) * 1e3
+    return {"mean_us": batch_us, "timing": "back-to-back batch of %d launches" % (4 * reps),
+            "each": {k: each[k] for k in ("mean_us", "median_us", "p10_us", "p90_us", "reps")}}
+
+
 # ---------------------------------------------------------------------------
 # Headline: decode projection set, H=7168
 # ---------------------------------------------------------------------------
@@ -305,8 +316,7 @@ def bench_decode(D, steps, warmup, log_reps):
         comp[name]["batch_mean_us"] = tb * 1e3
         comp[name]["batch_GBps"] = parts[name] / (tb * 1e-3) / 1e9
     for name in standalone(0):
-        t = time_each(D, lambda i, name=name: standalone(i)[name][0](), log_reps)
-        st = stats(t)
+        st = timed(D, lambda i, name=name: standalone(i)[name][0](), log_reps)
         b = standalone(0)[name][1]
         comp["separate_" + name] = {**st, "bytes": b, "GBps": b / (st["mean_us"] * 1e-6) / 1e9,
                                     "frac_hbm": b / (st["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -336,7 +346,7 @@ def bench_decode(D, steps, warmup, log_reps):
 
 
 # ---------------------------------------------------------------------------
-# Other workloads (each kernel timed with events)
+# Other workloads (each kernel: HIP events around a back-to-back batch, see timed)
 # ---------------------------------------------------------------------------
 def bench_gemv2048(D, reps):
     torch, q8 = D.torch, D.q8
@@ -347,9 +357,9 @@ def bench_gemv2048(D, reps):
     Ws = D.copies(W, n)
     aq, asd = q8.alloc_act(1, 2048, q8.LAYOUT_ROW)
     y = torch.empty(2048, device=D.dev)
-    tq = stats(time_each(D, lambda i: q8.q8_quantize(x, q8.LAYOUT_ROW, aq, asd), reps))
-    tg = stats(time_each(D, lambda i: q8.q8_gemv(Ws[i % n], aq, asd, y), reps))
-    tf = stats(time_each(D, lambda i: q8.q8_gemv_f32(Ws[i % n], x.view(-1), y), reps))
+    tq = timed(D, lambda i: q8.q8_quantize(x, q8.LAYOUT_ROW, aq, asd), reps)
+    tg = timed(D, lambda i: q8.q8_gemv(Ws[i % n], aq, asd, y), reps)
+    tf = timed(D, lambda i: q8.q8_gemv_f32(Ws[i % n], x.view(-1), y), reps)
     # back-to-back replay of many distinct-weight GEMVs: aggregate bytes / aggregate time
     R = min(n, 200)
     g = torch.cuda.CUDAGraph()
@@ -395,11 +405,14 @@ def gemm_entry(t, T, N, K):
 
 
 class Practical:
-    """Practical HBM ceilings of plain streams (q8_hbm_stream_probe) with a kernel's read/write mix
-    and total bytes, cold: regions of a 4 GiB pool rotate so that no launch finds its bytes in a
-    cache. The pattern is the one whose share of written bytes is nearest the kernel's: read-only
-    (0), two reads per write (1/3) or a copy (1/2)."""
-    GRID = (1024, 2048)
+    """Practical HBM ceilings of plain streams with a kernel's read/write mix and total bytes,
+    cold: regions of a 4 GiB pool rotate so that no launch finds its bytes in a cache. The
+    pattern is the one whose share of written bytes is nearest the kernel's: read-only (0; the
+    read probe q8_hbm_read_probe), two reads per write (1/3) or a copy (1/2) (the stream probe
+    q8_hbm_stream_probe). Timed as the kernels are: one pair of HIP events around a back-to-back
+    batch. The best of a few launch shapes is kept."""
+    READ_SHAPES = ((1024, 1), (2048, 1), (2048, 2), (4096, 2))
+    GRID = (1024, 2048, 4096)
 
     def __init__(self, D):
         self.D = D
@@ -412,7 +425,7 @@ class Practical:
         f = write_b / (read_b + write_b)
         return min((("read", 0.0), ("2read_1write", 1 / 3), ("copy", 0.5)), key=lambda p: abs(p[1] - f))[0]
 
-    def ceiling(self, read_b, write_b):
+    def ceiling(self, read_b, write_b, reps=10):
         torch, q8 = self.D.torch, self.D.q8
         pat = self.pattern(read_b, write_b)
         nstreams = {"read": 1, "2read_1write": 3, "copy": 2}[pat]
@@ -427,20 +440,22 @@ class Practical:
         nsets = max(2, min(math.ceil(COLD_BYTES / set_b), (4 << 30) // set_b))
         bufs = [[self.pool[k * set_b + j * stream_b:k * set_b + (j + 1) * stream_b] for j in range(nstreams)]
                 for k in range(nsets)]
+        shapes = self.READ_SHAPES if pat == "read" else [(w, 1) for w in self.GRID]
         best = None
-        for wgs in self.GRID:
-            def one(i, wgs=wgs):
+        for wgs, u in shapes:
+            def one(i, wgs=wgs, u=u):
                 b = bufs[i % nsets]
                 if pat == "read":
-                    q8.hbm_stream_probe(stream_b, wgs, src0=b[0], out=self.out)
+                    q8.hbm_read_probe(b[0], wgs, u, self.out)
                 elif pat == "copy":
                     q8.hbm_stream_probe(stream_b, wgs, src0=b[0], dst=b[1])
                 else:
                     q8.hbm_stream_probe(stream_b, wgs, src0=b[0], src1=b[1], dst=b[2])
-            t = stats(time_each(self.D, one, 10))
-            gbs = set_b / t["mean_us"] / 1e3
+            us = time_batch(self.D, one, 4 * reps) * 1e3
+            gbs = set_b / us / 1e3
             if best is None or gbs > best["GBps"]:
-                best = {"pattern": pat, "bytes": set_b, "GBps": gbs, "mean_us": t["mean_us"], "workgroups": wgs}
+                best = {"pattern": pat, "bytes": set_b, "GBps": gbs, "mean_us": us, "sets": nsets,
+                        "timing": "back-to-back batch", "workgroups": wgs, "loads_per_lane": u}
         self.cache[key] = best
         return best
 
@@ -457,7 +472,7 @@ def hbm_entry(t, b, warm=None, read_b=None):
         e["practical"] = c
         e["frac_of_practical"] = e["GBps"] / c["GBps"]
     if warm is not None:
-        e["warm"] = {"mean_us": warm["mean_us"], "median_us": warm["median_us"],
+        e["warm"] = {"mean_us": warm["mean_us"],
                      "GBps": b / warm["mean_us"] / 1e3, "frac_hbm": b / warm["mean_us"] / 1e3 / HBM_PEAK_GBS,
                      "note": "one set of buffers reused by every rep (may be served in part by the 256 MB "
                              "Infinity Cache); the headline figure above rotates distinct sets"}
@@ -499,8 +514,8 @@ def bench_prefill_rms(D, reps):
         xs, ys, qs, sd = sets[i % ns]
         q8.rmsnorm_quant(xs, w, EPS, q8.LAYOUT_PLANE64, ys, qs, sd)
 
-    t = stats(time_each(D, rms, reps))
-    tw = stats(time_each(D, lambda i: rms(0), reps))
+    t = timed(D, rms, reps)
+    tw = timed(D, lambda i: rms(0), reps)
     out["rmsnorm_quant_plane64"] = hbm_entry(t, b, tw, read_b=T * K * 4 + K * 4)
     out["rmsnorm_quant_plane64"]["sets"] = ns
     prod_us = t["mean_us"]
@@ -518,7 +533,7 @@ def bench_prefill_rms(D, reps):
         def one(i, n=n):
             _, _, qs, sd = sets[i % ns]
             q8.q8_gemm(wsets[i % ng][n], qs, sd, T, csets[i % ng][n])
-        t = stats(time_each(D, one, reps))
+        t = timed(D, one, reps)
         out[f"q8_gemm_{Ws[n].n}x{K}"] = gemm_entry(t, T, Ws[n].n, K)
         sep_us += t["mean_us"]
     # q, k and v over the one plane in one grouped launch (what the slice uses)
@@ -528,11 +543,11 @@ def bench_prefill_rms(D, reps):
         _, _, qs, sd = sets[i % ns]
         q8.q8_gemm_shared_multi([wsets[i % ng][n] for n in names], qs, sd, T, [csets[i % ng][n] for n in names])
 
-    t = stats(time_each(D, grouped, reps))
+    t = timed(D, grouped, reps)
     n_all = sum(W.n for W in Ws.values())
     out[f"q8_gemm_shared_multi_qkv_{n_all}x{K}"] = gemm_entry(t, T, n_all, K)
     out[f"q8_gemm_shared_multi_qkv_{n_all}x{K}"]["warm"] = {
-        "mean_us": stats(time_each(D, lambda i: grouped(0), reps))["mean_us"], "note": "one operand set"}
+        "mean_us": timed(D, lambda i: grouped(0), reps)["mean_us"], "note": "one operand set"}
     pq, ps = sets[0][2], sets[0][3]
     y = sets[0][1]
     C = csets[0]
@@ -562,10 +577,10 @@ def bench_prefill_swiglu(D, reps):
         (gi, ui), (yi, qi, si) = gs[i % 2], outs[i % 2]
         q8.swiglu_quant(gi, ui, q8.LAYOUT_PLANE64, yi if f32 else None, qi, si, f32=f32)
 
-    t = stats(time_each(D, sw, reps))
-    out["swiglu_quant_plane64"] = hbm_entry(t, b, stats(time_each(D, lambda i: sw(0), reps)), read_b=T * K * 8)
+    t = timed(D, sw, reps)
+    out["swiglu_quant_plane64"] = hbm_entry(t, b, timed(D, lambda i: sw(0), reps), read_b=T * K * 8)
     # plane only (y = NULL): for a down projection that reads no f32 activation
-    t3 = stats(time_each(D, lambda i: sw(i, False), reps))
+    t3 = timed(D, lambda i: sw(i, False), reps)
     b3 = b - T * K * 4
     out["swiglu_quant_plane64_no_f32"] = hbm_entry(t3, b3, read_b=T * K * 8)
     # the unfused form's quantize pass: q8_quantize of the f32 y into the same plane (bit-identical
@@ -580,8 +595,8 @@ def bench_prefill_swiglu(D, reps):
     def quant(i):
         q8.q8_quantize(ysets[i % nq], q8.LAYOUT_PLANE64, *qsets[i % nq])
 
-    t4 = stats(time_each(D, quant, reps))
-    out["q8_quantize_plane64"] = hbm_entry(t4, b4, stats(time_each(D, lambda i: quant(0), reps)), read_b=T * K * 4)
+    t4 = timed(D, quant, reps)
+    out["q8_quantize_plane64"] = hbm_entry(t4, b4, timed(D, lambda i: quant(0), reps), read_b=T * K * 4)
     del ysets[2:], qsets[2:]
     # the down GEMM: distinct (weights, plane, output) sets over >= 1 GB
     gb = gemm_min_bytes(T, N, K)
@@ -594,9 +609,9 @@ def bench_prefill_swiglu(D, reps):
     def gemm(i):
         q8.q8_gemm(Wset[i % ng], *Pset[i % ng], T, Cset[i % ng])
 
-    t2 = stats(time_each(D, gemm, reps))
+    t2 = timed(D, gemm, reps)
     out[f"q8_gemm_{N}x{K}"] = gemm_entry(t2, T, N, K)
-    out[f"q8_gemm_{N}x{K}"]["warm"] = {"mean_us": stats(time_each(D, lambda i: gemm(0), reps))["mean_us"],
+    out[f"q8_gemm_{N}x{K}"]["warm"] = {"mean_us": timed(D, lambda i: gemm(0), reps)["mean_us"],
                                        "note": "one operand set"}
     del Wset[1:], Pset[2:], Cset[1:]
     y, (pq, ps), C = outs[0][0], outs[0][1:], torch.empty((T, N), device=D.dev)
@@ -615,8 +630,7 @@ def bench_prefill_q4k(D, reps):
     x = D.tensor("prefill_rms", "x")
     w = D.tensor("prefill_rms", "w_norm")
     pq, ps = q8.alloc_act(T, K, q8.LAYOUT_PLANE64)
-    t = stats(time_each(D, lambda i: q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_PLANE64, None, pq, ps, f32=False),
-                        reps))
+    t = timed(D, lambda i: q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_PLANE64, None, pq, ps, f32=False), reps)
     out = {"rmsnorm_quant_plane64_no_f32": {**t, "bytes": rms_bytes(T, K, 1) - T * K * 4}}
     total_us = t["mean_us"]
     launches = counted_launches(q8, lambda: q8.rmsnorm_quant(x, w, EPS, q8.LAYOUT_PLANE64, None, pq, ps, f32=False))
@@ -624,7 +638,7 @@ def bench_prefill_q4k(D, reps):
         blocks = D.upload(synth.q4k_tensor("prefill_q4k", name))
         W = q8.Q4KWeights(blocks, K)
         C = torch.empty((T, W.n), device=D.dev)
-        tg = stats(time_each(D, lambda i: q8.q4k_gemm(W, pq, ps, T, C), reps))
+        tg = timed(D, lambda i: q8.q4k_gemm(W, pq, ps, T, C), reps)
         launches += counted_launches(q8, lambda: q8.q4k_gemm(W, pq, ps, T, C))
         e = gemm_entry(tg, T, W.n, K)
         e["min_bytes"] = T * K + (T // 64 + 1) * (K // 32) * 256 + blocks.numel() + T * W.n * 4
@@ -651,9 +665,9 @@ def bench_lm_head(D, reps):
     y1 = torch.empty_like(x1)
     aq, asd = q8.alloc_act(1, K, q8.LAYOUT_ROW)
     logits = torch.empty(N, device=D.dev)
-    t = stats(time_each(D, lambda i: q8.rmsnorm_quant(x1, w, EPS, q8.LAYOUT_ROW, y1, aq, asd), reps))
+    t = timed(D, lambda i: q8.rmsnorm_quant(x1, w, EPS, q8.LAYOUT_ROW, y1, aq, asd), reps)
     out["rmsnorm_quant_row_3584"] = {**t, "bytes": rms_bytes(1, K), "GBps": rms_bytes(1, K) / t["mean_us"] / 1e3}
-    tg = stats(time_each(D, lambda i: q8.q8_gemv(Ws[i % n], aq, asd, logits), reps))
+    tg = timed(D, lambda i: q8.q8_gemv(Ws[i % n], aq, asd, logits), reps)
     gb = gemv_bytes(N, K)
     out[f"q8_gemv_{N}x{K}"] = hbm_entry(tg, gb, read_b=gb - N * 4)
     out["t1_slice_tok_per_s_two_launches"] = 1.0 / ((t["mean_us"] + tg["mean_us"]) * 1e-6)
@@ -661,7 +675,7 @@ def bench_lm_head(D, reps):
     # the T=1 slice in one launch: the output norm and the LM-head GEMV
     def t1_step(i):
         q8.rmsnorm_quant_gemv_shared_multi_plus_f32(x1, w, EPS, [Ws[i % n]], None, None, y1, aq, asd, [logits])
-    ts = stats(time_each(D, t1_step, reps))
+    ts = timed(D, t1_step, reps)
     sb = rms_bytes(1, K) + gb - (K + (K // 32) * 4)  # the GEMV reads its activation from LDS
     out["rmsnorm_quant_gemv_1x3584_152064"] = {**ts, "bytes": sb, "GBps": sb / ts["mean_us"] / 1e3,
                                                "frac_hbm": sb / ts["mean_us"] / 1e3 / HBM_PEAK_GBS}
@@ -671,10 +685,10 @@ def bench_lm_head(D, reps):
     y512 = torch.empty_like(x512)
     pq, ps = q8.alloc_act(T, K, q8.LAYOUT_PLANE64)
     C = torch.empty((T, N), device=D.dev)
-    t = stats(time_each(D, lambda i: q8.rmsnorm_quant(x512, w, EPS, q8.LAYOUT_PLANE64, y512, pq, ps), reps))
+    t = timed(D, lambda i: q8.rmsnorm_quant(x512, w, EPS, q8.LAYOUT_PLANE64, y512, pq, ps), reps)
     out["rmsnorm_quant_plane64_512"] = {**t, "bytes": rms_bytes(T, K, 1),
                                         "GBps": rms_bytes(T, K, 1) / t["mean_us"] / 1e3}
-    t2 = stats(time_each(D, lambda i: q8.q8_gemm(Ws[i % n], pq, ps, T, C), max(3, reps // 2)))
+    t2 = timed(D, lambda i: q8.q8_gemm(Ws[i % n], pq, ps, T, C), max(3, reps // 2))
     out[f"q8_gemm_{N}x{K}_T512"] = gemm_entry(t2, T, N, K)
     out["t512_slice_launches"] = {"predicted": 2, "counted": counted_launches(q8, lambda: (
         q8.rmsnorm_quant(x512, w, EPS, q8.LAYOUT_PLANE64, y512, pq, ps), q8.q8_gemm(Ws[0], pq, ps, T, C)))}
@@ -785,16 +799,16 @@ def hbm_reference(D, mib=2048, reps=5):
     out_words = torch.empty(65536, dtype=torch.int32, device=D.dev)
     sweep = {}
     for wgs, u in PROBE_GRID:
-        t = stats(time_each(D, lambda i, wgs=wgs, u=u: q8.hbm_read_probe(src, wgs, u, out_words), reps))
+        t = timed(D, lambda i, wgs=wgs, u=u: q8.hbm_read_probe(src, wgs, u, out_words), reps)
         sweep[f"{wgs}wg_x{u}"] = {"mean_us": t["mean_us"], "GBps": n * 4 / t["mean_us"] / 1e3}
     best = max(sweep, key=lambda k: sweep[k]["GBps"])
     dst = torch.empty_like(src)
-    tc = stats(time_each(D, lambda i: dst.copy_(src), reps))
+    tc = timed(D, lambda i: dst.copy_(src), reps)
     # the stream probe (q8_hbm_stream_probe) on the same buffers: writes only, and one read per write
     nb = n * 4
-    tw = min((stats(time_each(D, lambda i, w=w: q8.hbm_stream_probe(nb, w, dst=dst), reps)) for w in Practical.GRID),
+    tw = min((timed(D, lambda i, w=w: q8.hbm_stream_probe(nb, w, dst=dst), reps) for w in Practical.GRID),
              key=lambda t: t["mean_us"])
-    tp = min((stats(time_each(D, lambda i, w=w: q8.hbm_stream_probe(nb, w, src0=src, dst=dst), reps))
+    tp = min((timed(D, lambda i, w=w: q8.hbm_stream_probe(nb, w, src0=src, dst=dst), reps)
               for w in Practical.GRID), key=lambda t: t["mean_us"])
     out = {"read_GBps": sweep[best]["GBps"], "read_bytes": n * 4, "read_launch": best,
            "read_kernel": "q8_hbm_read_probe (k_read_probe): 16-byte grid-stride loads, one pass, "
