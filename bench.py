@@ -462,6 +462,18 @@ class Practical:
 
 PRACTICAL = None  # set in main()
 
+# The (read, written) bytes per launch of the bandwidth-bound kernels above: the decode step
+# (165 MB read), rmsnorm_quant and q8_quantize PLANE64, swiglu_quant PLANE64 with and without
+# its f32 output, and the LM-head GEMV.
+PRACTICAL_MIXES = [
+    (165260032, 0),
+    (3325 * 3584 * 4 + 3584 * 4, rms_bytes(3325, 3584, 1) - 3325 * 3584 * 4 - 3584 * 4),
+    (3325 * 18944 * 4, quant_bytes(3325, 18944, 1) - 3325 * 18944 * 4),
+    (3325 * 18944 * 8, swiglu_bytes(3325, 18944, 1) - 3325 * 18944 * 8),
+    (3325 * 18944 * 8, swiglu_bytes(3325, 18944, 1) - 3325 * 18944 * 12),
+    (gemv_bytes(152064, 3584) - 152064 * 4, 152064 * 4),
+]
+
 
 def hbm_entry(t, b, warm=None, read_b=None):
     """A bandwidth-bound kernel's rate; warm: the same kernel on one set of buffers. read_b: the
@@ -873,7 +885,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--reps", type=int, default=20, help="timed launches per kernel in the per-config section")
     ap.add_argument("--configs", default="all",
-                    help="comma list of: decode,gemv2048,prefill_rms,prefill_swiglu,lm_head,prefill_q4k")
+                    help="comma list of: decode,gemv2048,prefill_rms,prefill_swiglu,lm_head,prefill_q4k; "
+                         "or ceilings (the practical HBM ceilings only)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall-clock budget of the oracle CPU baseline")
     args = ap.parse_args()
@@ -890,6 +903,13 @@ def main():
         else set(args.configs.split(","))
     global PRACTICAL
     PRACTICAL = Practical(D)
+    if "ceilings" in which:  # the practical ceilings alone (for a trace of the probes)
+        hbm = hbm_reference(D)
+        for read_b, write_b in PRACTICAL_MIXES:
+            PRACTICAL.ceiling(read_b, write_b)
+        hbm["practical_ceilings"] = sorted(PRACTICAL.cache.values(), key=lambda c: (c["pattern"], c["bytes"]))
+        print(json.dumps({"hbm_reference": hbm}), flush=True)
+        return
     if "decode" not in which:  # profiling a subset: no headline line
         for name, fn in (("gemv2048", bench_gemv2048), ("prefill_rms", bench_prefill_rms),
                          ("prefill_swiglu", bench_prefill_swiglu), ("lm_head", bench_lm_head),
