@@ -11,7 +11,10 @@
 namespace q8 {
 namespace {
 
-enum Dst : int { kDstNone = 0, kDstRow = 1, kDstPlane = 2 };
+// kDstStage: ROW addressing into a workgroup's LDS staging rows (row t of the
+// workgroup's consecutive rows at t modulo its row count), written out as plane
+// tiles by the caller.
+enum Dst : int { kDstNone = 0, kDstRow = 1, kDstPlane = 2, kDstStage = 3 };
 
 // Streaming accesses: the non-temporal bit, so the line does not displace
 // others from L2 and the MALL. Measured per stream, not applied wholesale:
@@ -43,7 +46,7 @@ __device__ __forceinline__ void store_stream(void* p, const uint4& v) {
 template <int D>
 __device__ __forceinline__ void store_quant(const Quant8& r, int64_t t, int c, int e, int K, int nb, int8_t* qs,
                                             uint32_t* sd) {
-    if constexpr (D == kDstRow) {
+    if constexpr (D == kDstRow || D == kDstStage) {
         *reinterpret_cast<uint32_t*>(qs + t * K + (int64_t)c * kQK + e) = r.qs4;
         if (e == 0) sd[t * nb + c] = r.sd;
     } else if constexpr (D == kDstPlane) {
@@ -104,8 +107,10 @@ __device__ __forceinline__ float rms_row_total(float ss, float* buf, bool& any_b
 // the same index of w. Writes y (unless NULL) and the quantized output of row
 // t. part, part2: WAVES floats of LDS each (the two passes' partial sums).
 // Every wave of the workgroup must call it.
-template <int D, int NV, int WPR, int WAVES>
-__device__ __forceinline__ void rms_finish(float4 (&v)[NV], const float4 (&wv)[NV], float eps,
+// wv: the same indices of w, as a float4[NV] in registers or as WLds (read
+// from LDS where used).
+template <int D, int NV, int WPR, int WAVES, typename WV>
+__device__ __forceinline__ void rms_finish(float4 (&v)[NV], const WV& wv, float eps,
                                            float* __restrict__ y, int64_t t, int64_t rows, int64_t tpad, int K,
                                            int nb, int8_t* __restrict__ qs, uint32_t* __restrict__ sd, float* part,
                                            float* part2) {
@@ -163,16 +168,25 @@ __device__ __forceinline__ void rms_finish(float4 (&v)[NV], const float4 (&wv)[N
         v[k] = o;  // zero for padded rows and past K
     }
     if constexpr (D != kDstNone) {
+        const int64_t tq = D == kDstStage ? t % (WAVES / WPR) : t;  // the staging row
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int c = (li + kStride * k) >> 3;
             if (c < nb) {
                 const Quant8 r = quantize_block8(v[k]);
-                store_quant<D>(r, t, c, (lane & 7) * 4, K, nb, qs, sd);
+                store_quant<D>(r, tq, c, (lane & 7) * 4, K, nb, qs, sd);
             }
         }
     }
 }
+
+// w held in LDS (K float4-indexed values, zero past K): element k of a lane's
+// share is read where it is used.
+template <int WPR>
+struct WLds {
+    const float4* base;  // this lane's first element: w4 + li
+    __device__ __forceinline__ float4 operator[](int k) const { return base[kWave * WPR * k]; }
+};
 
 // Loads of row t's share (see rms_finish): x from clamped, always-valid
 // addresses (padded rows read row 0), w the same indices.
