@@ -137,6 +137,32 @@ def test_quantize_ieee_division_blocks(layout):
         check_act_exact(pq, psd, x, layout, f"plane-only swiglu_quant divide blocks {rows}x{K}")
 
 
+@pytest.mark.parametrize("layout", [ROW, PLANE])
+def test_quantize_amax_sweep_bit_exact(layout):
+    """The block maximum swept over f32's whole range (65,536 bit patterns from the smallest
+    subnormal to the largest finite value, so the scale d = amax/127 takes every exponent:
+    f32-subnormal, f16-subnormal, ordinary and f16-overflowing), each block's other 31 values a
+    random fraction of it: bit-exact with the oracle (the division by 127, the reciprocal path
+    and its IEEE fallback, the f16 rounding of d)."""
+    rng = np.random.default_rng(4242)
+    n = 65536
+    bits = rng.integers(1, 0x7F7FFFFF, size=n, dtype=np.uint32)
+    # and the ends of each range: the smallest subnormals, the subnormal/normal boundary,
+    # the largest finite value
+    bits[:6] = [0x00000001, 0x00000002, 0x007FFFFF, 0x00800000, 0x00800001, 0x7F7FFFFF]
+    amax = np.sort(bits).view(np.float32)
+    frac = rng.uniform(-1.0, 1.0, size=(n, 32))
+    x = (amax[:, None].astype(np.float64) * frac).astype(np.float32)
+    pos = rng.integers(0, 32, size=n)
+    sign = np.where(rng.random(n) < 0.5, -1.0, 1.0).astype(np.float32)
+    x[np.arange(n), pos] = amax * sign
+    assert np.all(np.abs(x).max(axis=1) == amax)
+    x = x.reshape(2048, 1024)
+    qs, sd = quantize_dev(up(x), 2048, 1024, layout)
+    torch.cuda.synchronize()
+    check_act_exact(qs, sd, x, layout, f"amax sweep layout {layout}")
+
+
 def test_quantize_random_many_rows_bit_exact():
     x = synth.normal((333, 3584), stream=3300, std=3.0)
     qs, sd = quantize_dev(up(x), 333, 3584, ROW)
