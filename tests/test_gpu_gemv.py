@@ -227,6 +227,36 @@ def test_gemv_f32_quantizes_with_ieee_division(pad_to):
     assert np.array_equal(ref, exact)
 
 
+def test_gemv_f32_quantize_amax_sweep():
+    """The one-lane quantize inside q8_gemv_f32 with block maxima swept over the range whose
+    f16 scale is finite (4,096 patterns from the smallest subnormal to 8.3e6, in 16 activations
+    of K=8192), identity weights as above: y = f16(d_a) * q_a exactly, equal to the oracle's
+    quantize. (A block whose scale overflows f16 stores d = infinity, and every GEMV output then
+    takes 0 * infinity = NaN from it, in the oracle's GEMV too; the quantize itself is checked up
+    to the largest finite f32 in test_gpu_producers.)"""
+    K = 8192
+    rng = np.random.default_rng(4343)
+    top = int(np.float32(8.3e6).view(np.uint32))  # d = amax/127 stays below f16's maximum
+    bits = rng.integers(1, top, size=16 * (K // 32), dtype=np.uint32)
+    bits[:6] = [0x00000001, 0x00000002, 0x007FFFFF, 0x00800000, 0x00800001, top]
+    amax = np.sort(bits).view(np.float32).reshape(16, K // 32)
+    wq = np.eye(K, dtype=np.int8)
+    wd = np.full((K, K // 32), 0x3C00, np.uint16)
+    W = q8lib.Q8Weights(up(wq), up(wd.view(np.int16)))
+    for i in range(16):
+        frac = rng.uniform(-1.0, 1.0, size=(K // 32, 32))
+        x = (amax[i][:, None].astype(np.float64) * frac).astype(np.float32)
+        x[np.arange(K // 32), rng.integers(0, 32, size=K // 32)] = amax[i]
+        x = x.reshape(1, K)
+        y = poisoned(K, torch.float32, 0xFF)
+        q8lib.q8_gemv_f32(W, up(x).view(-1), y)
+        torch.cuda.synchronize()
+        qo, do, _ = oracle.quantize(x)
+        exact = oracle.f16_to_f64(do[0])[np.arange(K) // 32] * qo[0].astype(np.float64)
+        assert np.all(np.isfinite(exact))
+        assert np.array_equal(to_np(y).astype(np.float64), exact), f"activation {i}"
+
+
 # q8_gemv_shared_multi_plus_f32: (grouped member Ns, K) with (f32 part Nx, Kx), and the
 # launches it must make: one for the shapes with a pair kernel, two for the others
 # (grouped K <= 2048, f32 K > 512), one when a part is empty.
