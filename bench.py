@@ -321,6 +321,11 @@ def bench_decode(D, steps, warmup, log_reps):
         comp["separate_" + name] = {**st, "bytes": b, "GBps": b / (st["mean_us"] * 1e-6) / 1e9,
                                     "frac_hbm": b / (st["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                     "launches_per_step": 0}
+        if name.startswith("q8_gemv") and b > 10e6 and PRACTICAL is not None:
+            # a weight stream: the read ceiling at its own size (outputs are under 0.1% of it)
+            c = PRACTICAL.ceiling(b, 0)
+            comp["separate_" + name]["practical"] = c
+            comp["separate_" + name]["frac_of_practical"] = comp["separate_" + name]["GBps"] / c["GBps"]
     del g
     # the same step with one weight copy, resident in the 256 MB Infinity Cache ("warm")
     gw = torch.cuda.CUDAGraph()
