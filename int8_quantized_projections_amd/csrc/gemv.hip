@@ -52,8 +52,8 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (W >= 4) v += dpp_f<kDppQuadXor2>(v);
     if constexpr (W >= 8) v += dpp_f<kDppRowHalfMirror>(v);
     if constexpr (W >= 16) v += dpp_f<kDppRowMirror>(v);
-    if constexpr (W >= 32) v += __shfl_xor(v, 16);
-    if constexpr (W >= 64) v += __shfl_xor(v, 32);
+    if constexpr (W >= 32) v = add_xor16(v);
+    if constexpr (W >= 64) v = add_xor32(v);
     return v;
 }
 

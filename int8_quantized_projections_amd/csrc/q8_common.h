@@ -82,15 +82,31 @@ constexpr float kHalfMargin = 0.5f - 0x1p-14f;
 // True when d is a nonzero f32-subnormal: the reciprocal bound above needs a normal d.
 __device__ __forceinline__ bool subnormal_nonzero(float d) { return fbits(d) - 1u < 0x007FFFFFu; }
 
+// v plus the value of lane i ^ 16 (add_xor16) or i ^ 32 (add_xor32), with
+// gfx950's v_permlane16_swap / v_permlane32_swap: the swap of 16-lane rows
+// 0<->1 and 2<->3 (of the two 32-lane halves) in VALU registers, where a lane
+// shuffle is an LDS round trip. The two operands come out as (lower row's,
+// upper row's) in both rows, so the sum has the bits of v + shfl_xor(v, 16)
+// (resp. 32) in every lane (f32 addition is commutative).
+__device__ __forceinline__ float add_xor16(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
 // Sum over all 64 lanes with a fixed tree; every lane receives the same bits.
 __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_f<kDppQuadXor1>(v);
     v += dpp_f<kDppQuadXor2>(v);
     v += dpp_f<kDppRowHalfMirror>(v);
     v += dpp_f<kDppRowMirror>(v);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    v = add_xor16(v);
+    return add_xor32(v);
 }
 
 __device__ __forceinline__ uint32_t f16_bits(float d) {
