@@ -353,6 +353,17 @@ def bench_decode(D, steps, warmup, log_reps):
 # ---------------------------------------------------------------------------
 # Other workloads (each kernel: HIP events around a back-to-back batch, see timed)
 # ---------------------------------------------------------------------------
+def launch_floor(D, reps):
+    """The back-to-back time per launch of a kernel that does almost nothing (the read probe over
+    16 KB, one workgroup): the floor under any kernel's time in a batch of launches."""
+    torch, q8 = D.torch, D.q8
+    buf = torch.zeros(16384, dtype=torch.uint8, device=D.dev)
+    out = torch.empty(1, dtype=torch.int32, device=D.dev)
+    us = time_batch(D, lambda i: q8.hbm_read_probe(buf, 1, 1, out), 4 * reps) * 1e3
+    return {"mean_us": us, "kernel": "k_read_probe<1>, 16 KB, one workgroup",
+            "timing": "back-to-back batch of %d launches" % (4 * reps)}
+
+
 def bench_gemv2048(D, reps):
     torch, q8 = D.torch, D.q8
     wl = "gemv_2048"
@@ -383,11 +394,10 @@ def bench_gemv2048(D, reps):
     fb = gemv_f32_bytes(2048, 2048)
     return {
         "slice_launches": {"predicted": 1, "counted": counted_launches(q8, lambda: q8.q8_gemv_f32(Ws[0], x.view(-1), y))},
-        "q8_gemv_f32_2048x2048": {**tf, "bytes": fb, "GBps": fb / tf["mean_us"] / 1e3,
-                                  "frac_hbm": fb / tf["mean_us"] / 1e3 / HBM_PEAK_GBS, "launches": 1},
+        "q8_gemv_f32_2048x2048": {**hbm_entry(tf, fb, read_b=fb - 2048 * 4), "launches": 1},
         "q8_quantize_2048": {**tq, "bytes": quant_bytes(1, 2048), "GBps": quant_bytes(1, 2048) / tq["mean_us"] / 1e3},
-        "q8_gemv_2048x2048": {**tg, "bytes": gb, "GBps": gb / tg["mean_us"] / 1e3,
-                              "frac_hbm": gb / tg["mean_us"] / 1e3 / HBM_PEAK_GBS},
+        "q8_gemv_2048x2048": hbm_entry(tg, gb, read_b=gb - 2048 * 4),
+        "launch_floor": launch_floor(D, reps),
         "q8_gemv_2048x2048_graph_back_to_back": {"us_per_gemv": agg_us, "GBps": gb / agg_us / 1e3,
                                                  "frac_hbm": gb / agg_us / 1e3 / HBM_PEAK_GBS, "gemvs": R},
     }
@@ -416,7 +426,7 @@ class Practical:
     read probe q8_hbm_read_probe), two reads per write (1/3) or a copy (1/2) (the stream probe
     q8_hbm_stream_probe). Timed as the kernels are: one pair of HIP events around a back-to-back
     batch. The best of a few launch shapes is kept."""
-    READ_SHAPES = ((1024, 1), (2048, 1), (2048, 2), (4096, 2))
+    READ_SHAPES = ((256, 1), (512, 1), (1024, 1), (2048, 1), (2048, 2), (4096, 2))
     GRID = (1024, 2048, 4096)
 
     def __init__(self, D):
