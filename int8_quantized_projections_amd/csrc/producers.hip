@@ -292,7 +292,41 @@ __global__ __launch_bounds__(WAVES * 64) void k_rmsnorm(const float* __restrict_
 constexpr int kStageRows = 8;
 constexpr int kStageMaxK = 4096;  // two waves x 64 lanes x 8 float4
 
-template <int NV>
+// The balanced form, for up to 4096 padded rows (at most two of these
+// workgroups per CU): a kernel that moves every byte once is held to a CU's
+// share of the chip's bandwidth, so its time follows the most-loaded CU. With
+// 8 rows per workgroup, 3328 rows are 416 workgroups: 160 CUs carry 16 rows and
+// 96 carry 8 (measured: 2048 rows 14.2 us, 2560 rows 21.6 us, 3328 rows
+// 24.8 us). Here the row pairs are dealt evenly to the CUs instead: CU c holds
+// P or P + 1 pairs, up to 4 of them in workgroup c and the rest in workgroup
+// c + kCUs (the first kCUs workgroups of a grid take one CU each before any CU
+// takes a second), so no CU carries more than 2 * ceil(tpad / 512) rows, and a
+// CU's first workgroup is full before its second takes rows (up to 2048 rows
+// the second workgroups have none and exit). A workgroup's rows are
+// contiguous, an even count of at most 8 starting at an even row, so the plane
+// runs stay 64-byte aligned.
+constexpr int kCUs = 256;                             // MI355X
+constexpr int64_t kBalMaxRows = 2 * kCUs * kStageRows;  // 4096
+
+// First row s and row count n of workgroup b of the balanced grid (2 * kCUs).
+__device__ __forceinline__ void bal_rows(int b, int64_t tpad, int64_t& s, int& n) {
+    const int u = (int)(tpad / 2);  // row pairs
+    const int P = u / kCUs, r = u % kCUs;
+    auto first = [](int p) { return 2 * min(p, kStageRows / 2); };       // rows of a CU's first workgroup, p pairs
+    auto second = [](int p) { return 2 * max(p - kStageRows / 2, 0); };  // and of its second
+    if (b < kCUs) {
+        s = (int64_t)min(b, r) * first(P + 1) + (int64_t)max(0, b - r) * first(P);
+        n = first(b < r ? P + 1 : P);
+    } else {
+        const int c = b - kCUs;
+        s = (int64_t)r * first(P + 1) + (int64_t)(kCUs - r) * first(P) + (int64_t)min(c, r) * second(P + 1) +
+            (int64_t)max(0, c - r) * second(P);
+        n = second(c < r ? P + 1 : P);
+    }
+}
+
+// BAL: the balanced rows above; else 8 consecutive rows per workgroup.
+template <int NV, bool BAL>
 __global__ __launch_bounds__(1024) void k_rmsnorm_plane8(const float* __restrict__ x, const float* __restrict__ w,
                                                          float eps, float* __restrict__ y, int64_t rows,
                                                          int64_t tpad, int K, int nb, int8_t* __restrict__ qs,
@@ -303,34 +337,52 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_plane8(const float* __restrict
     __shared__ __attribute__((aligned(16))) float4 st_w[kStageMaxK / 4];
     __shared__ float part[kWaves], part2[kWaves];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int64_t wg = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int64_t t = wg * kStageRows + wave / 2;
+    int64_t s0;  // this workgroup's rows: s0 .. s0+n-1, staged in LDS at row % 8
+    int n;
+    if constexpr (BAL) {
+        bal_rows(blockIdx.x, tpad, s0, n);
+        if (n == 0) return;  // the whole workgroup: no barrier is left waiting
+    } else {
+        s0 = xcd_contiguous(blockIdx.x, gridDim.x) * kStageRows;
+        n = kStageRows;
+    }
+    // a row slot past the workgroup's rows computes nothing it writes (t = tpad)
+    const int64_t t = wave / 2 < n ? s0 + wave / 2 : tpad;
     // w once per workgroup, in LDS: one 1 KB copy per wave (bytes past K read as zeros),
     // so a lane holds only its x in registers (two workgroups fit a CU)
     q8gemm::lds_copy16(q8gemm::make_rsrc(w, (int64_t)K * 4), (uint32_t)(lane * 16), (uint32_t)(wave * 1024),
                        reinterpret_cast<int8_t*>(st_w) + wave * 1024);
     float4 v[NV];
-    rms_load_x<NV, 2>(v, x, t, rows, K);
+    if (t < rows) {  // wave-uniform: padded and unused slots load nothing (their values are zeroed)
+        rms_load_x<NV, 2>(v, x, t, rows, K);
+    } else {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     q8gemm::wait_copies();
     __syncthreads();
     const WLds<2> wl{st_w + (wave % 2) * kWave + lane};
     rms_finish<kDstStage, NV, 2, kWaves>(v, wl, eps, y, t, rows, tpad, K, nb, st_q, st_d, part, part2);
     __syncthreads();
-    // rows t0 .. t0+7 (t0 a multiple of 8, tpad of 64): rows r0 .. r0+7 of token group g
-    const int64_t t0 = wg * kStageRows, g = t0 >> 6;
-    const int r0 = (int)(t0 & 63);
-    // chunk c's 8 rows are 256 contiguous bytes of tile (g, c); piece i = (c, row, half)
-    // in destination order, each half taken from the source half it holds after the swizzle
+    // chunk c of rows s0 .. s0+n-1 is a run of 32n contiguous bytes of a plane tile (of two
+    // tiles when the rows cross a 64-token group); piece i = (c, row slot, half) in destination
+    // order, each half taken from the source half it holds after the swizzle
     for (int i = (int)threadIdx.x; i < nb * kStageRows * 2; i += 1024) {
-        const int c = i / (kStageRows * 2), r = (i >> 1) % kStageRows, hd = i & 1;
-        const int row = r0 + r;
-        const int hs = hd ^ (((row >> 2) ^ (row >> 3)) & 1);
-        const uint4 v = *reinterpret_cast<const uint4*>(st_q + r * K + c * kQK + hs * 16);
-        store_stream(qs + (g * nb + c) * kTileBytes + row * kQK + hd * 16, v);
+        const int c = i / (kStageRows * 2), j = (i >> 1) % kStageRows, hd = i & 1;
+        if (j < n) {
+            const int64_t tt = s0 + j, g = tt >> 6;
+            const int row = (int)(tt & 63);
+            const int hs = hd ^ (((row >> 2) ^ (row >> 3)) & 1);
+            const uint4 q = *reinterpret_cast<const uint4*>(st_q + (int)(tt % kStageRows) * K + c * kQK + hs * 16);
+            store_stream(qs + (g * nb + c) * kTileBytes + row * kQK + hd * 16, q);
+        }
     }
     for (int i = (int)threadIdx.x; i < nb * kStageRows; i += 1024) {
-        const int c = i / kStageRows, r = i % kStageRows;
-        sd[(g * nb + c) * kGroup + r0 + r] = st_d[r * nb + c];
+        const int c = i / kStageRows, j = i % kStageRows;
+        if (j < n) {
+            const int64_t tt = s0 + j;
+            sd[((tt >> 6) * nb + c) * kGroup + (tt & 63)] = st_d[(int)(tt % kStageRows) * nb + c];
+        }
     }
 }
 
@@ -473,11 +525,24 @@ void dispatch_rms(hipStream_t s, const float* x, const float* w, float eps, floa
     if constexpr (D == kDstPlane) {
         // many rows held in registers: 8 rows per workgroup, the plane written in whole slices
         if (wpr == 2 && (nv == 4 || nv == 8) && k <= kStageMaxK) {
-            const dim3 sgrid((unsigned)(tpad / kStageRows)), block(2 * kStageRows * 64);
+            const dim3 block(2 * kStageRows * 64);
+            if (tpad <= kBalMaxRows) {  // rows dealt evenly to the CUs, two workgroups each
+                const dim3 bgrid((unsigned)(2 * kCUs));
+                if (nv == 4)
+                    q8h::launch_kernel(k_rmsnorm_plane8<4, true>, bgrid, block, 0, s, x, w, eps, y, rows, tpad, k,
+                                       nb, qs, sd);
+                else
+                    q8h::launch_kernel(k_rmsnorm_plane8<8, true>, bgrid, block, 0, s, x, w, eps, y, rows, tpad, k,
+                                       nb, qs, sd);
+                return;
+            }
+            const dim3 sgrid((unsigned)(tpad / kStageRows));
             if (nv == 4)
-                q8h::launch_kernel(k_rmsnorm_plane8<4>, sgrid, block, 0, s, x, w, eps, y, rows, tpad, k, nb, qs, sd);
+                q8h::launch_kernel(k_rmsnorm_plane8<4, false>, sgrid, block, 0, s, x, w, eps, y, rows, tpad, k, nb,
+                                   qs, sd);
             else
-                q8h::launch_kernel(k_rmsnorm_plane8<8>, sgrid, block, 0, s, x, w, eps, y, rows, tpad, k, nb, qs, sd);
+                q8h::launch_kernel(k_rmsnorm_plane8<8, false>, sgrid, block, 0, s, x, w, eps, y, rows, tpad, k, nb,
+                                   qs, sd);
             return;
         }
     }

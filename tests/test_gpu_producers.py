@@ -222,12 +222,17 @@ def _rms_case(rows, K, layout, stream):
 
 # rows <= 16 run one 1024-thread workgroup per row (K/4 > 8192 float4: the two-pass form), more rows 4 or 2
 # waves per row; from 1024 rows, PLANE64 with 4 or 8 float4 per lane (K in (1024, 4096]) takes the form
-# with 8 rows per workgroup and the plane staged in LDS (1027 and 1030 rows: ragged, padded to 1088)
+# with the plane staged in LDS: up to 4096 padded rows dealt evenly to 512 workgroups (even counts of 2 to
+# 8 rows, runs that cross 64-token groups; 1027 and 1030 rows: ragged, padded to 1088; 2049 rows: 2112,
+# 4 or 6 rows per workgroup; 2500 rows: 2560; 4033 rows: 4096, 8 rows each), beyond that 8 rows per
+# workgroup (4097 rows)
 @pytest.mark.parametrize("rows,K,layout", [(1, 7168, ROW), (1, 3584, ROW), (3, 640, ROW), (70, 896, PLANE),
                                            (130, 3584, PLANE), (64, 256, PLANE), (3, 9216, ROW), (65, 18944, PLANE),
                                            (2, 40960, ROW), (16, 2048, PLANE), (17, 2048, PLANE), (1, 32, ROW),
                                            (1027, 2048, PLANE), (1030, 2080, PLANE), (1100, 4096, PLANE),
-                                           (1025, 992, PLANE), (1024, 4128, PLANE), (1027, 3584, ROW)])
+                                           (1025, 992, PLANE), (1024, 4128, PLANE), (1027, 3584, ROW),
+                                           (2049, 2048, PLANE), (2500, 4096, PLANE), (4033, 1056, PLANE),
+                                           (4097, 2048, PLANE)])
 def test_rmsnorm_quant(rows, K, layout):
     x, w, y, qs, sd, y2, q2, s2 = _rms_case(rows, K, layout, 3400 + K + rows)
     ref = oracle.rmsnorm_f64(x, w, 1e-6)
@@ -345,7 +350,7 @@ def test_rmsnorm_input_domain(K, copies, layout):
     """RMSNorm over f32's range: y within 1e-5 relative of the oracle's f64 value plus FLT_MIN,
     the plane bit-exact with the oracle's quantize of that y, and rows with a finite sum of
     squares bit-identical to the same rows normalized among ordinary ones. copies > 1 gives
-    1080 rows, two rows per workgroup (eight with the plane staged, at K = 2048), so overflowing and
+    1080 rows, two rows per workgroup (four or six with the plane staged, at K = 2048), so overflowing and
     ordinary rows share workgroups (the rows <= 16 and K = 40960 cases take the 16-wave and the
     two-pass forms)."""
     x = np.tile(_domain_rows(K), (copies, 1))
