@@ -74,7 +74,12 @@ __device__ __forceinline__ int wsw(int r) {
 // DWL: the weight scales of a stage are copied into LDS with 4-byte copies of
 // block pairs, which needs K/32 even (4-byte aligned pairs); otherwise every
 // lane loads its own row's scales into registers one stage ahead.
-template <bool DWL>
+// HV: 32-token halves of the plane group per workgroup. 2: the 64-token tile.
+// 1: one half (two workgroups per 64-token tile), for grids with too few
+// 64-token tiles to give every SIMD more than one wave; each output element is
+// accumulated by the same instructions in the same order, so the bits are the
+// same.
+template <bool DWL, int HV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm(
     const int8_t* __restrict__ aq, const uint32_t* __restrict__ asd, const GemmMembers M, int64_t T, int K, int nb,
     int n_tiles, int64_t tiles) {
@@ -86,8 +91,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     // the first read of every stage wait for all copies of the next stage, and
     // no copy overlapped the compute: 8% slower on 3325x3584x18944, 22% on
     // N=512.)
+    static_assert(HV == 1 || HV == 2, "one or two 32-token halves");
     constexpr int kW = DWL ? kBN * kKT / 2 : 1;
-    __shared__ __attribute__((aligned(16))) int8_t lds_a0[kKT * kTileBytes], lds_a1[kKT * kTileBytes];
+    constexpr int kAB = HV * kTileBytes / 2;  // A bytes per block in LDS
+    __shared__ __attribute__((aligned(16))) int8_t lds_a0[kKT * kAB], lds_a1[kKT * kAB];
     __shared__ __attribute__((aligned(16))) int8_t lds_b0[kBN * kKT * kQK], lds_b1[kBN * kKT * kQK];
     __shared__ __attribute__((aligned(16))) uint32_t lds_s0[kKT * kGroup], lds_s1[kKT * kGroup];
     __shared__ __attribute__((aligned(16))) uint32_t lds_w0[kW], lds_w1[kW];
@@ -103,6 +110,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     int nt;
     int64_t g;
     tile_of(blockIdx.x, tiles, n_tiles, nt, g);
+    int h0 = 0;  // HV == 1: the workgroup's half of plane group g
+    if constexpr (HV == 1) {
+        h0 = (int)(g & 1);
+        g >>= 1;
+    }
     // the member this tile belongs to (wave-uniform) and the tile inside it
     int mi = 0, tbase = 0;
 #pragma unroll
@@ -131,10 +143,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     // LDS byte offsets of this lane's A fragments (token 32h + lane%32, half khalf)
     // and of its B fragment of block 0 (the XOR with wsw is linear in the block,
     // so block kb is at boff ^ (32 * kb)).
-    int aoff[2];
+    int aoff[HV];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int i = 32 * h + (lane & 31);
+    for (int h = 0; h < HV; ++h) {
+        const int i = 32 * h + (lane & 31);  // token in the LDS copy (HV == 1: in the half)
         aoff[h] = i * 32 + (((khalf ^ (i >> 2) ^ (i >> 3)) & 1) * 16);
     }
     const int boff = brow * kRowB + 16 * (khalf ^ wsw(brow));
@@ -145,9 +157,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     // Opaque to the optimiser: held in 16 VGPRs for the whole kernel instead of
     // being re-created from scalar registers before the MFMAs of every stage.
     asm volatile("" : "+v"(bias));
-    float acc[2][16];
+    float acc[HV][16];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < HV; ++h)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[h][i] = 0.0f;
 
@@ -166,7 +178,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const __amdgpu_buffer_rsrc_t r_s = make_rsrc(splane, (int64_t)nb * kGroup * 4);
     const __amdgpu_buffer_rsrc_t r_b = make_rsrc(wq + n0 * (int64_t)K, (N - n0) * (int64_t)K);
     const __amdgpu_buffer_rsrc_t r_w = make_rsrc(wd + n0 * (int64_t)nb, (N - n0) * (int64_t)nb * 2);
-    const uint32_t aoffs = (uint32_t)(wave * 1024 + lane * 16);  // + 4096 * it
+    // HV == 2: copy `it` of wave w fills LDS bytes 4096 it + 1024 w .. of the stage (blocks 2it and
+    // 2it + 1); HV == 1: wave w copies half h0 of block w
+    const uint32_t aoffs = (uint32_t)(HV == 2 ? wave * 1024 + lane * 16 : wave * kTileBytes + h0 * 1024 + lane * 16);
     const uint32_t soffs = (uint32_t)(wave * kGroup + lane) * 4;
     // weights: wave w copies tile rows 32w .. 32w+31, 64/kPR rows per instruction
     auto brow_of = [&](int it) { return 32 * wave + (64 / kPR) * it + lane / kPR; };
@@ -184,7 +198,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const int c0 = st * kKT;
         if (c0 + kKT <= nb) {
 #pragma unroll
-            for (int it = 0; it < kKT * kTileBytes / 16 / 256; ++it)
+            for (int it = 0; it < kKT * kAB / 16 / 256; ++it)
                 lds_copy16(r_a, aoffs, (uint32_t)(c0 * kTileBytes + it * 4096), &lds_a(b)[it * 4096 + wave * 1024]);
             if (wave < kKT) lds_copy4(r_s, soffs, (uint32_t)(c0 * kGroup * 4), &lds_s(b)[wave * kGroup]);
 #pragma unroll
@@ -194,10 +208,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 if (wave < kKT) lds_copy4(r_w, woffs, (uint32_t)(c0 * 2), &lds_w(b)[wave * 64]);
         } else {
 #pragma unroll
-            for (int it = 0; it < kKT * kTileBytes / 16 / 256; ++it) {
-                const int c = min(c0 + 2 * it + wave / 2, nb - 1);  // chunk of this wave's piece
-                lds_copy16(r_a, (uint32_t)(c * kTileBytes + (wave & 1) * 1024 + lane * 16), 0u,
-                           &lds_a(b)[it * 4096 + wave * 1024]);
+            for (int it = 0; it < kKT * kAB / 16 / 256; ++it) {
+                if constexpr (HV == 2) {
+                    const int c = min(c0 + 2 * it + wave / 2, nb - 1);  // chunk of this wave's piece
+                    lds_copy16(r_a, (uint32_t)(c * kTileBytes + (wave & 1) * 1024 + lane * 16), 0u,
+                               &lds_a(b)[it * 4096 + wave * 1024]);
+                } else {
+                    const int c = min(c0 + wave, nb - 1);
+                    lds_copy16(r_a, (uint32_t)(c * kTileBytes + h0 * 1024 + lane * 16), 0u, &lds_a(b)[wave * 1024]);
+                }
             }
             if (wave < kKT)
                 lds_copy4(r_s, (uint32_t)((min(c0 + wave, nb - 1) * kGroup + lane) * 4), 0u, &lds_s(b)[wave * kGroup]);
@@ -247,19 +266,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const int8_t* la = &lds_a(buf)[0];
         const int8_t* lb = &lds_b(buf)[0];
         const uint32_t* ls = &lds_s(buf)[0];
-        auto frags = [&](int kb, v4i (&af)[2], v4i& bf, uint32_t (&sc)[2]) {
+        auto frags = [&](int kb, v4i (&af)[HV], v4i& bf, uint32_t (&sc)[HV]) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                af[h] = *reinterpret_cast<const v4i*>(la + kb * kTileBytes + aoff[h]);
-                sc[h] = ls[kb * kGroup + 32 * h + srow];
+            for (int h = 0; h < HV; ++h) {
+                af[h] = *reinterpret_cast<const v4i*>(la + kb * kAB + aoff[h]);
+                sc[h] = ls[kb * kGroup + 32 * (HV == 2 ? h : h0) + srow];
             }
             bf = *reinterpret_cast<const v4i*>(lb + (boff ^ (32 * kb)));
         };
-        // Pipeline over the 2*kKT (block, half) tiles: the MFMA of the next tile
+        // Pipeline over the HV*kKT (block, half) tiles: the MFMA of the next tile
         // is issued before the epilogue of the current one, and the fragments of
         // block kb+1 are read from LDS while block kb is being finished.
-        v4i af[2], an[2], bf, bn;
-        uint32_t sc[2], sn[2];
+        v4i af[HV], an[HV], bf, bn;
+        uint32_t sc[HV], sn[HV];
         frags(0, af, bf, sc);
         v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[0], bf, bias, 0, 0, 0);
 #pragma unroll
@@ -272,19 +291,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             asm volatile("" : "+v"(dw));
             const float nbias = -kBiasF * dw;
             if (kb + 1 < kKT) frags(kb + 1, an, bn, sn);
-            // tile (kb, 0) is in d; start (kb, 1)
-            const v16i d0 = d;
-            d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[1], bf, bias, 0, 0, 0);
-            epilogue(acc[0], __builtin_bit_cast(v16f, d0), dw, nbias, f16_value(sc[0]));
-            // tile (kb, 1) is in d; start (kb + 1, 0)
-            const v16i d1 = d;
-            if (kb + 1 < kKT) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(an[0], bn, bias, 0, 0, 0);
-            epilogue(acc[1], __builtin_bit_cast(v16f, d1), dw, nbias, f16_value(sc[1]));
-            af[0] = an[0];
-            af[1] = an[1];
+            if constexpr (HV == 2) {
+                // tile (kb, 0) is in d; start (kb, 1)
+                const v16i d0 = d;
+                d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[1], bf, bias, 0, 0, 0);
+                epilogue(acc[0], __builtin_bit_cast(v16f, d0), dw, nbias, f16_value(sc[0]));
+                // tile (kb, 1) is in d; start (kb + 1, 0)
+                const v16i d1 = d;
+                if (kb + 1 < kKT) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(an[0], bn, bias, 0, 0, 0);
+                epilogue(acc[1], __builtin_bit_cast(v16f, d1), dw, nbias, f16_value(sc[1]));
+            } else {
+                // block kb is in d; start kb + 1
+                const v16i d0 = d;
+                if (kb + 1 < kKT) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(an[0], bn, bias, 0, 0, 0);
+                epilogue(acc[0], __builtin_bit_cast(v16f, d0), dw, nbias, f16_value(sc[0]));
+            }
+#pragma unroll
+            for (int h = 0; h < HV; ++h) {
+                af[h] = an[h];
+                sc[h] = sn[h];
+            }
             bf = bn;
-            sc[0] = sn[0];
-            sc[1] = sn[1];
         }
     };
     auto lds_dw = [&](int buf, h2 (&db)[kKT / 2]) {
@@ -327,10 +354,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
     if (nvalid) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < HV; ++h) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t t = g * kGroup + 32 * h + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                const int64_t t = g * kGroup + 32 * (HV == 2 ? h : h0) + 8 * (r >> 2) + 4 * khalf + (r & 3);
                 if (t < T) C[t * ldc + nrow] = acc[h][r];
             }
         }
@@ -340,6 +367,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 }  // namespace
 
 namespace {
+
+// A launch takes 32-token halves when every half-tile workgroup then has a CU
+// of its own (2 x 64-token tiles <= the 256 CUs). Measured, bit-identical:
+// 16 tiles (100x1024x4096) 32.1 -> 24.2 us, 32 tiles (512x512x3584) 28.9 ->
+// 21.9 us; 208 tiles (3325x512x3584) 31.8 -> 30.9 us, 224 (512x3584x3584)
+// 32.8 -> 33.0 us, and 448 or more tiles 10-17% slower, where the halves share
+// CUs and each CU pulls more bytes per output.
+constexpr int64_t kHalfTileMax = 128;
 
 // Validation shared by q8_gemm and q8_gemm_shared_multi (the activation side is
 // checked by the caller).
@@ -394,14 +429,20 @@ int launch_gemm(int counter, int m, const q8_weights* const* W, const int8_t* a_
         M.ldc[j] = M.ldc[M.m - 1];
         M.tile0[j + 1] = (int)n_tiles;
     }
-    const int64_t tiles = n_tiles * q8h::ceil_div(t, kGroup);
+    // A grid of few 64-token tiles leaves most CUs idle: then each workgroup
+    // takes one 32-token half of a tile (the same per-element arithmetic and
+    // bits, twice the workgroups).
+    const bool half = n_tiles * q8h::ceil_div(t, kGroup) <= kHalfTileMax;
+    const int64_t tiles = n_tiles * q8h::ceil_div(t, half ? kGroup / 2 : kGroup);
     if (tiles > INT32_MAX) return Q8_ESHAPE;
+    auto go = [&](auto kernel) {
+        q8h::launch_kernel(kernel, dim3((unsigned)tiles), dim3(256), 0, stream, a_qs, a_sd, M, t, (int)W[0]->k, nb,
+                           (int)n_tiles, tiles);
+    };
     if (pairs)
-        q8h::launch_kernel(k_gemm<true>, dim3((unsigned)tiles), dim3(256), 0, stream, a_qs, a_sd, M, t,
-                           (int)W[0]->k, nb, (int)n_tiles, tiles);
+        half ? go(k_gemm<true, 1>) : go(k_gemm<true, 2>);
     else
-        q8h::launch_kernel(k_gemm<false>, dim3((unsigned)tiles), dim3(256), 0, stream, a_qs, a_sd, M, t,
-                           (int)W[0]->k, nb, (int)n_tiles, tiles);
+        half ? go(k_gemm<false, 1>) : go(k_gemm<false, 2>);
     return q8h::launch_status(counter);
 }
 

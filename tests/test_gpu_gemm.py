@@ -153,3 +153,25 @@ def test_gemm_shared_multi_matches_separate_and_oracle(T, K, Ns):
         if n:
             r, norm = oracle.gemm(ref[i][0], ref[i][1], qo, do)
             assert_norm(g[:T, :n], r, norm, 1e-5, f"grouped member {i} N={n}")
+
+
+@pytest.mark.parametrize("T", [130, 97])
+def test_gemm_half_tile_form_bit_identical_to_full_tiles(T):
+    """A launch of at most 128 64-token tiles runs one workgroup per 32-token half of a tile, a larger
+    one a workgroup per tile: the same matrix computed both ways (alone, and grouped with a wide
+    member that makes the grid large) gives the same bits, and matches the oracle."""
+    K = 640
+    x = synth.normal((T, K), stream=5900 + T)
+    pq, ps, qo, do, _ = plane_act(x)
+    small, wq, wd = weights(synth.normal((200, K), stream=5901, std=0.02))
+    wide, _, _ = weights(synth.normal((8192, K), stream=5902, std=0.02))
+    alone = run_gemm(small, pq, ps, T, ldc=203, rows=T + 1)  # 2 x 3 tiles: halves
+    grouped = [poisoned((T + 1) * 203, torch.float32, 0xFF).view(T + 1, 203),
+               poisoned(T * 8192, torch.float32, 0xFF).view(T, 8192)]
+    q8lib.q8_gemm_shared_multi([small, wide], pq, ps, T, grouped, [203, 8192])  # 66 x 3 tiles: whole tiles
+    torch.cuda.synchronize()
+    a, g = to_np(alone), to_np(grouped[0])
+    assert np.array_equal(a[:T, :200].view(np.uint32), g[:T, :200].view(np.uint32))
+    assert np.all(np.isnan(a[:T, 200:])) and np.all(np.isnan(a[T:, :]))
+    ref, norm = oracle.gemm(wq, wd, qo, do)
+    assert_norm(a[:T, :200], ref, norm, 1e-5, f"gemm half-tile form {T}x200x{K}")
