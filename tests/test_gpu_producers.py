@@ -375,3 +375,24 @@ def test_producers_deterministic():
     a = _rms_case(130, 3584, PLANE, 3600)
     b = _rms_case(130, 3584, PLANE, 3600)
     assert torch.equal(a[2], b[2]) and torch.equal(a[3], b[3]) and torch.equal(a[4], b[4])
+
+
+def test_rmsnorm_plane64_forms_bit_identical():
+    """From 1024 rows, rmsnorm_quant PLANE64 deals up to 4096 padded rows evenly to the CUs and takes 8
+    rows per workgroup beyond. Every row's bits depend on the row, K and the waves per row (two in both
+    forms) only: the first rows of one input give the same y, quantized blocks and scales whether the
+    call has 1100 or 3325 rows (balanced) or 4200 rows (8-row workgroups)."""
+    K = 2048
+    x = synth.normal((4200, K), stream=3810)
+    w = synth.normal((K,), stream=3811, mean=1.0, std=0.1)
+    out = {}
+    for n in (4200, 3325, 1100):
+        y, qs, sd = q8lib.rmsnorm_quant(up(x[:n]), up(w), 1e-6, PLANE)
+        torch.cuda.synchronize()
+        q, d16, s, bad = oracle.decode_plane64(to_np(qs), to_np(sd).view(np.uint32), n, K)
+        assert bad == 0, f"{n} rows: padded tail not zero"
+        out[n] = (to_np(y), q, d16, s)
+    for n in (3325, 1100):
+        for a, b, what in zip(out[n], out[4200], ("y", "qs", "d", "ssum")):
+            assert np.array_equal(a.view(np.uint8) if a.dtype == np.float32 else a,
+                                  (b[:n].view(np.uint8) if b.dtype == np.float32 else b[:n])), f"{n} rows: {what}"
