@@ -281,14 +281,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_rmsnorm(const float* __restrict_
     rmsnorm_rows<D, NV, WPR, WAVES>(x, w, eps, y, rows, tpad, K, nb, qs, sd, xcd_contiguous(blockIdx.x, gridDim.x));
 }
 
-// rmsnorm_quant into the PLANE64 layout for many rows: 16 waves, 8
+// rmsnorm_quant into the PLANE64 layout for many rows: 16 waves, up to 8
 // consecutive rows per workgroup, two waves per row with the row in registers
-// (rmsnorm_rows: the same arithmetic and bits as the 4-wave form). The rows'
-// quantized blocks and scale words are staged in LDS and written as whole
-// 256-byte slices of the plane tiles and 32-byte runs of scale words: written
-// straight from each row, every block is one 32-byte piece and one 4-byte
-// word, 2 KB and 256 bytes from the row's next block (measured: 27.4 us for
-// 3325x3584, of which 6 us for the 13.4 MB of plane).
+// (rms_finish: the same arithmetic and bits as the other two-wave forms). The
+// rows' quantized blocks and scale words are staged in LDS and written as runs
+// of the plane tiles (a 256-byte slice for 8 rows) and runs of scale words:
+// written straight from each row, every block is one 32-byte piece and one
+// 4-byte word, 2 KB and 256 bytes from the row's next block (measured: 27.4 us
+// for 3325x3584, of which 6 us for the 13.4 MB of plane).
 constexpr int kStageRows = 8;
 constexpr int kStageMaxK = 4096;  // two waves x 64 lanes x 8 float4
 
