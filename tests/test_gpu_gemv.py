@@ -205,7 +205,7 @@ def test_gemv_f32_equals_quantize_then_gemv(N, K):
 
 @pytest.mark.parametrize("pad_to", [256, 2048])
 def test_gemv_f32_quantizes_with_ieee_division(pad_to):
-    """The one-lane quantize inside q8_gemv_f32 on blocks where the IEEE quotient x/d and a
+    """The quantize inside q8_gemv_f32 on blocks where the IEEE quotient x/d and a
     reciprocal multiply round to different integers. The weights are the identity with unit
     scales (qs = 1 on the diagonal, d = f16 1.0), so y[n] = f16(d_a) * q_a[n] exactly and every
     activation value shows in the output: y must equal the oracle's quantize bit for bit."""
@@ -228,7 +228,7 @@ def test_gemv_f32_quantizes_with_ieee_division(pad_to):
 
 
 def test_gemv_f32_quantize_amax_sweep():
-    """The one-lane quantize inside q8_gemv_f32 with block maxima swept over the range whose
+    """The quantize inside q8_gemv_f32 with block maxima swept over the range whose
     f16 scale is finite (4,096 patterns from the smallest subnormal to 8.3e6, in 16 activations
     of K=8192), identity weights as above: y = f16(d_a) * q_a exactly, equal to the oracle's
     quantize. (A block whose scale overflows f16 stores d = infinity, and every GEMV output then
@@ -297,3 +297,43 @@ def test_gemv_pair_bit_identical_to_separate_calls(Ns, K, Nx, Kx, launches):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"member {i} of {Ns}x{K}"
         if Nx:
             assert torch.equal(yx.view(torch.int32), ref_x.view(torch.int32)), f"f32 part {Nx}x{Kx}"
+
+
+def test_pair_f32_part_one_lane_quantize_edges():
+    """The f32 part of the pair launch (and of the one-launch decode step) quantizes its activation
+    with the one-lane form: one lane holds a whole 32-value block. Through the pair, with identity
+    weights of unit scales (y[n] = f16(d_a) * q_a[n] exactly): the blocks where the IEEE quotient
+    x/d and a reciprocal multiply round to different integers, then block maxima swept from the
+    smallest subnormal to 8.3e6; every output equal to the oracle's quantize, bit for bit."""
+    Kx = 512
+    wq = np.eye(Kx, dtype=np.int8)
+    wd = np.full((Kx, Kx // 32), 0x3C00, np.uint16)
+    Wx = q8lib.Q8Weights(up(wq), up(wd.view(np.int16)))
+    Ws = [weights(synth.normal((64, 3584), stream=4780, std=0.02))[0]]
+    aq, asd = q8lib.q8_quantize(up(synth.normal((1, 3584), stream=4781)), q8lib.LAYOUT_ROW)
+    rng = np.random.default_rng(4782)
+    acts = []
+    blocks = divide_blocks_f32().reshape(-1)
+    x = synth.normal((1, Kx), stream=4783)[0].copy()
+    x[: blocks.size] = blocks
+    acts.append(x)
+    top = int(np.float32(8.3e6).view(np.uint32))
+    bits = np.sort(rng.integers(1, top, size=64 * (Kx // 32), dtype=np.uint32))
+    bits[:4] = [0x00000001, 0x007FFFFF, 0x00800000, top]
+    for amax in np.sort(bits).view(np.float32).reshape(64, Kx // 32):
+        frac = rng.uniform(-1.0, 1.0, size=(Kx // 32, 32))
+        xb = (amax[:, None].astype(np.float64) * frac).astype(np.float32)
+        xb[np.arange(Kx // 32), rng.integers(0, 32, size=Kx // 32)] = amax
+        acts.append(xb.reshape(-1))
+    ys = [poisoned(64, torch.float32, 0xFF)]
+    for i, xa in enumerate(acts):
+        xa = xa.reshape(1, Kx).astype(np.float32)
+        yx = poisoned(Kx, torch.float32, 0xFF)
+        q8lib.launch_counts_reset()
+        q8lib.q8_gemv_shared_multi_plus_f32(Ws, aq, asd, Wx, up(xa).view(-1), ys, yx)
+        torch.cuda.synchronize()
+        assert q8lib.launch_counts()["q8_gemv_shared_multi_plus_f32"] == 1
+        qo, do, _ = oracle.quantize(xa)
+        exact = oracle.f16_to_f64(do[0])[np.arange(Kx) // 32] * qo[0].astype(np.float64)
+        assert np.all(np.isfinite(exact))
+        assert np.array_equal(to_np(yx).astype(np.float64), exact), f"activation {i}"
