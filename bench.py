@@ -188,7 +188,7 @@ def timed(D, fn, reps):
     each = stats(time_each(D, fn, reps))
     batch_us = time_batch(D, fn, 4 * reps) * 1e3
     return {"mean_us": batch_us, "timing": "back-to-back batch of %d launches" % (4 * reps),
-            "each": {k: each[k] for k in ("mean_us", "median_us", "p10_us", "p90_us", "reps")}}
+            "each": {k: each[k] for k in ("mean_us", "median_us", "p10_us", "p90_us", "reps", "reps_us")}}
 
 
 # ---------------------------------------------------------------------------
