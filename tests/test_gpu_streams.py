@@ -1,0 +1,86 @@
+"""Every entry point enqueues on the stream it is given (the C ABI's stream argument; the binding
+passes torch's current stream) and on no other.
+
+Each call runs on a side stream while the default stream is held by a long spin kernel, into a
+freshly poisoned output that is read back on the side stream: a kernel put on the default stream
+would still be waiting behind the spin, and the read would return the poison. The results must be
+bit-identical to the same calls made beforehand on the default stream. (If the side stream is one
+that waits for the default stream, the check only runs slower: it cannot fail when the library is
+right.)
+"""
+import pytest
+
+import synth
+from _gpu import ensure_built, poisoned, up, weights
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+ensure_built()
+from int8_quantized_projections_amd import q8lib  # noqa: E402
+
+ROW, PLANE = q8lib.LAYOUT_ROW, q8lib.LAYOUT_PLANE64
+SPIN_CYCLES = int(2.4e9 * 0.05)  # about 50 ms of the default stream
+
+
+def _calls():
+    """name -> function(outputs) writing into the given poisoned outputs, and the output shapes."""
+    x = up(synth.normal((130, 2048), stream=6000))
+    g, u = up(synth.normal((130, 2048), stream=6001)), up(synth.normal((130, 2048), stream=6002))
+    w = up(synth.normal((2048,), stream=6003, mean=1.0, std=0.1))
+    W = weights(synth.normal((300, 2048), stream=6004, std=0.02))[0]
+    W2 = weights(synth.normal((64, 2048), stream=6005, std=0.02))[0]
+    Wx = weights(synth.normal((96, 128), stream=6006, std=0.02))[0]
+    x1 = up(synth.normal((1, 2048), stream=6007))
+    x128 = up(synth.normal((128,), stream=6008))
+    aq, asd = q8lib.q8_quantize(x1, ROW)
+    pq, ps = q8lib.q8_quantize(x, PLANE)
+    nq_r, ns_r = q8lib.act_bytes(130, 2048, ROW)
+    nq_p, ns_p = q8lib.act_bytes(130, 2048, PLANE)
+    torch.cuda.synchronize()
+
+    def fresh(spec):
+        return [poisoned(n, dt) for n, dt in spec]
+
+    return {
+        "q8_quantize": ([(nq_p, torch.int8), (ns_p // 4, torch.int32)],
+                        lambda o: q8lib.q8_quantize(x, PLANE, o[0], o[1])),
+        "rmsnorm_quant": ([(130 * 2048, torch.float32), (nq_p, torch.int8), (ns_p // 4, torch.int32)],
+                          lambda o: q8lib.rmsnorm_quant(x, w, 1e-6, PLANE, o[0].view(130, 2048), o[1], o[2])),
+        "swiglu_quant": ([(130 * 2048, torch.float32), (nq_r, torch.int8), (ns_r // 4, torch.int32)],
+                         lambda o: q8lib.swiglu_quant(g, u, ROW, o[0].view(130, 2048), o[1], o[2])),
+        "q8_gemv": ([(300, torch.float32)], lambda o: q8lib.q8_gemv(W, aq, asd, o[0])),
+        "q8_gemv_f32": ([(300, torch.float32)], lambda o: q8lib.q8_gemv_f32(W, x1.view(-1), o[0])),
+        "q8_gemv_shared_multi": ([(300, torch.float32), (64, torch.float32)],
+                                 lambda o: q8lib.q8_gemv_shared_multi([W, W2], aq, asd, o)),
+        "q8_gemm": ([(130 * 300, torch.float32)], lambda o: q8lib.q8_gemm(W, pq, ps, 130, o[0].view(130, 300))),
+        "rmsnorm_quant_gemv_shared_multi_plus_f32": (
+            [(2048, torch.float32), (2048, torch.int8), (64, torch.int32), (300, torch.float32),
+             (64, torch.float32), (96, torch.float32)],
+            lambda o: q8lib.rmsnorm_quant_gemv_shared_multi_plus_f32(
+                x1, w, 1e-6, [W, W2], Wx, x128, o[0].view(1, 2048), o[1], o[2], [o[3], o[4]], o[5])),
+    }, fresh
+
+
+@pytest.mark.parametrize("name", ["q8_quantize", "rmsnorm_quant", "swiglu_quant", "q8_gemv", "q8_gemv_f32",
+                                  "q8_gemv_shared_multi", "q8_gemm",
+                                  "rmsnorm_quant_gemv_shared_multi_plus_f32"])
+def test_call_runs_on_the_given_stream(name):
+    calls, fresh = _calls()
+    spec, call = calls[name]
+    ref = fresh(spec)
+    call(ref)
+    torch.cuda.synchronize()
+    ref = [t.cpu() for t in ref]
+    side = torch.cuda.Stream()
+    out = fresh(spec)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SPIN_CYCLES)  # the default stream is busy from here on
+    with torch.cuda.stream(side):
+        call(out)
+        got = [t.cpu() for t in out]  # copies on the side stream, which wait for its work only
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(got, ref)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{name}: output {i} differs"
