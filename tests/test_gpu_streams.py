@@ -8,6 +8,7 @@ bit-identical to the same calls made beforehand on the default stream. (If the s
 that waits for the default stream, the check only runs slower: it cannot fail when the library is
 right.)
 """
+import numpy as np
 import pytest
 
 import synth
@@ -34,6 +35,7 @@ def _calls():
     W2 = weights(synth.normal((64, 2048), stream=6005, std=0.02))[0]
     Wx = weights(synth.normal((96, 128), stream=6006, std=0.02))[0]
     x1 = up(synth.normal((1, 2048), stream=6007))
+    W4 = q8lib.Q4KWeights(up(np.ascontiguousarray(synth.q4k_blocks(256, 2048, 6009))), 2048)
     x128 = up(synth.normal((128,), stream=6008))
     aq, asd = q8lib.q8_quantize(x1, ROW)
     pq, ps = q8lib.q8_quantize(x, PLANE)
@@ -56,6 +58,13 @@ def _calls():
         "q8_gemv_shared_multi": ([(300, torch.float32), (64, torch.float32)],
                                  lambda o: q8lib.q8_gemv_shared_multi([W, W2], aq, asd, o)),
         "q8_gemm": ([(130 * 300, torch.float32)], lambda o: q8lib.q8_gemm(W, pq, ps, 130, o[0].view(130, 300))),
+        "q8_gemm_shared_multi": ([(130 * 300, torch.float32), (130 * 64, torch.float32)],
+                                 lambda o: q8lib.q8_gemm_shared_multi([W, W2], pq, ps, 130,
+                                                                      [o[0].view(130, 300), o[1].view(130, 64)])),
+        "q4k_gemm": ([(130 * 256, torch.float32)], lambda o: q8lib.q4k_gemm(W4, pq, ps, 130, o[0].view(130, 256))),
+        "q8_gemv_shared_multi_plus_f32": ([(300, torch.float32), (64, torch.float32), (96, torch.float32)],
+                                          lambda o: q8lib.q8_gemv_shared_multi_plus_f32([W, W2], aq, asd, Wx, x128,
+                                                                                        [o[0], o[1]], o[2])),
         "rmsnorm_quant_gemv_shared_multi_plus_f32": (
             [(2048, torch.float32), (2048, torch.int8), (64, torch.int32), (300, torch.float32),
              (64, torch.float32), (96, torch.float32)],
@@ -65,7 +74,8 @@ def _calls():
 
 
 @pytest.mark.parametrize("name", ["q8_quantize", "rmsnorm_quant", "swiglu_quant", "q8_gemv", "q8_gemv_f32",
-                                  "q8_gemv_shared_multi", "q8_gemm",
+                                  "q8_gemv_shared_multi", "q8_gemv_shared_multi_plus_f32", "q8_gemm",
+                                  "q8_gemm_shared_multi", "q4k_gemm",
                                   "rmsnorm_quant_gemv_shared_multi_plus_f32"])
 def test_call_runs_on_the_given_stream(name):
     calls, fresh = _calls()
