@@ -554,3 +554,41 @@ def test_q4k_degenerate_blocks():
     w = oracle.q4k_dequant(no_min, 1, K)[0]
     a = qa[0].astype(np.float64) * np.repeat(oracle.f16_to_f64(da[0]), 32)
     assert ref2[0, 0] == pytest.approx(float(np.dot(w, a)), rel=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Thread count
+# ---------------------------------------------------------------------------
+
+
+def test_oracle_results_do_not_depend_on_thread_count():
+    """The oracle's parallel loops split work over rows, columns or blocks only; every output is
+    computed by one thread in a fixed order, so one thread and all of them give the same bits
+    (the benchmark times it both ways)."""
+    x = synth.normal((70, 640), stream=9100)
+    w = synth.normal((640,), stream=9101, mean=1.0, std=0.1)
+    wq, wd = oracle.gguf_to_planar(oracle.quantize_weights_gguf(synth.normal((200, 640), stream=9102, std=0.02)),
+                                   200, 640)
+    blocks = synth.q4k_blocks(64, 512, 9103)
+    x4 = synth.normal((70, 512), stream=9104)
+
+    def run():
+        q, d, s = oracle.quantize(x)
+        y = oracle.rmsnorm_f64(x, w, 1e-6)
+        g = oracle.gemv(wq, wd, q[3], d[3])
+        c = oracle.gemm(wq, wd, q, d)
+        q4, d4, s4 = oracle.quantize(x4)
+        k = oracle.q4k_gemm(blocks, 64, 512, q4, d4, s4)
+        return [q, d, s, y, g[0], c[0], k[0]]
+
+    n = oracle.num_threads()
+    try:
+        oracle.set_threads(1)
+        one = run()
+        oracle.set_threads(max(n, 4))
+        many = run()
+    finally:
+        oracle.set_threads(n)
+    for i, (a, b) in enumerate(zip(one, many)):
+        a, b = np.asarray(a), np.asarray(b)
+        assert a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"output {i}"
