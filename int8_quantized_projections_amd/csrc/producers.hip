@@ -523,7 +523,8 @@ void dispatch_rms(hipStream_t s, const float* x, const float* w, float eps, floa
         return;
     }
     if constexpr (D == kDstPlane) {
-        // many rows held in registers: 8 rows per workgroup, the plane written in whole slices
+        // many rows held in registers: up to 8 rows per workgroup, the plane staged in LDS and
+        // written in runs
         if (wpr == 2 && (nv == 4 || nv == 8) && k <= kStageMaxK) {
             const dim3 block(2 * kStageRows * 64);
             if (tpad <= kBalMaxRows) {  // rows dealt evenly to the CUs, two workgroups each
