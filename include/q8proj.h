@@ -228,9 +228,9 @@ int q8_gemv(const q8_weights* W, const int8_t* a_qs, const uint32_t* a_sd, float
  * so launches should be removed; for an activation with a single consumer the
  * quantize moves into that consumer). x: [K] f32, 16-byte aligned, with
  * K = W->k <= 8192 (Q8_ESHAPE otherwise; wider activations are quantized once
- * with q8_quantize). Every wave quantizes the blocks it holds with the
- * q8_quantize arithmetic, so y is bit-identical to q8_quantize(x) followed by
- * q8_gemv(W, ...). y: [N] f32.
+ * with q8_quantize). Each workgroup quantizes x once into its shared memory
+ * with the q8_quantize arithmetic, so y is bit-identical to q8_quantize(x)
+ * followed by q8_gemv(W, ...). y: [N] f32.
  */
 int q8_gemv_f32(const q8_weights* W, const float* x, float* y, void* stream);
 
